@@ -1,0 +1,18 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP path")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests fail loudly (not skip) when run without a GPU: the marker
+    # selection (-m gpu / -m "not gpu") decides what runs where.
+    pass
