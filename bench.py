@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache attention forward pass on one MI355X.
+
+One step = one whole forward call of the MHA decode workload (32 q = 32 kv
+heads x 128, fp16, page size 16): the new token of every sequence is appended
+into its page, then every sequence attends over its cache (context 4096 + the
+new token), batch 256.  Inputs are seeded synthetic data resident in HBM
+before timing starts.  `value` is the whole-job decode rate in GB/s of
+algorithmic bytes (the K/V rows the method must read, q, out, lse, the table
+entries and metadata, plus the appended rows read and written).
+
+Printed as ONE JSON line, with
+  roofline     the attention kernel alone: algorithmic bytes per launch over
+               its mean launch time (HIP events on the launch stream), against
+               the 8 TB/s HBM peak;
+  cpu_baseline the CPU fp64 oracle timed on the host on a bounded sample of
+               the same workload (whole sequences), scaled to GB/s;
+  prefill      the causal-prefill-with-append workload (batch 4 x 2048 new
+               tokens, 32 x 128, fp16, empty cache) in TFLOP/s of causal
+               attention flops against the 2.5 PFLOP/s dense fp16 MFMA peak.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFS = 2500.0
+METRIC = "paged-attn decode HBM GB/s + prefill TFLOP/s, as fraction of MI355X peak"
+
+
+def algorithmic_bytes(case, elt=2):
+    """Bytes the method must move for one call (visible K/V, q, out, lse,
+    table entries, metadata; plus append traffic)."""
+    Kb = case.keys_visible()
+    hkv, hq, d = case.num_heads_kv, case.num_heads_q, case.head_dim
+    T = case.total_q
+    P = case.page_size or 1
+    b = sum(Kb) * hkv * d * 2 * elt
+    b += T * hq * d * elt * 2 + T * hq * 4
+    if case.page_size:
+        b += sum(-(-k // P) for k in Kb) * 4
+    b += (2 * case.batch + 1) * 4
+    if case.append:
+        b += 2 * T * hkv * d * elt * 2
+    return b
+
+
+def causal_flops(case):
+    """4 * D * Hq * sum over query rows of the keys each row can see."""
+    total = 0
+    for L, n in zip(case.cache_seqlens, case.q_lens):
+        K = L + (n if case.append else 0)
+        if case.causal:
+            # rows i = 0..n-1 see K - n + i + 1 keys
+            total += n * (K - n) + n * (n + 1) // 2
+        else:
+            total += n * K
+    return 4 * case.head_dim * case.num_heads_q * total
+
+
+def time_calls(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps     # ms per call
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--ctx", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence / kv head / key range, see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_lds_amd as pa
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.cuda.get_device_properties(0)
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+
+    # ---- headline: MHA decode step (append + attend) ----
+    case = wl.mha_decode(args.batch, args.ctx, page_size=16, append=True)
+    case.causal = False
+    log(f"bench: generating {case.name} on {dev.name}")
+    inp = wl.make_inputs(case, "cuda")
+    out = torch.empty_like(inp.q)
+    lse = torch.empty(inp.q.shape[0], inp.q.shape[1], dtype=torch.float32, device="cuda")
+    args_c = pa.make_args(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens,
+                          inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q,
+                          max_seqlen_k=inp.max_seqlen_k, k_new=inp.k_new, v_new=inp.v_new,
+                          out=out, softmax_lse=lse)
+    splits = pa.paged_attn_splits_for(args_c)
+    ws_bytes = pa.paged_attn_workspace_size(args_c)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        pa.paged_attn_fwd(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens,
+                          inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q,
+                          max_seqlen_k=inp.max_seqlen_k, k_new=inp.k_new, v_new=inp.v_new,
+                          out=out, softmax_lse=lse, workspace=ws)
+
+    log(f"bench: splits={splits}, timing {args.steps} steps after {args.warmup} warmup")
+    torch.cuda.synchronize()
+    ms = time_calls(step, args.steps, args.warmup, torch)
+    step_bytes = algorithmic_bytes(case)
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    # ---- roofline of the attention kernel alone: same visible keys, no append ----
+    seq_after = inp.cache_seqlens + 1          # the appended token is now in the cache
+    attn_case = wl.Case(**{**case.__dict__, "append": False,
+                           "cache_seqlens": [L + 1 for L in case.cache_seqlens]})
+
+    def attn_only():
+        pa.paged_attn_fwd(inp.q, inp.k_cache, inp.v_cache, inp.block_table, seq_after,
+                          inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q,
+                          max_seqlen_k=inp.max_seqlen_k, out=out, softmax_lse=lse, workspace=ws)
+
+    attn_ms = time_calls(attn_only, args.steps, args.warmup, torch)
+    attn_bytes = algorithmic_bytes(attn_case)
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "attn_fwd_kernel<f16,128>", "launch_ms": round(attn_ms, 4),
+                "bytes_per_launch": attn_bytes, "splits": splits}
+
+    # ---- CPU baseline: the oracle on a bounded sample of whole sequences ----
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        torch.cuda.synchronize()
+
+        def sample(nseq):
+            pages = [torch.from_numpy(np.asarray(inp.pages_of[b], dtype=np.int64)) for b in range(nseq)]
+            flat = torch.cat(pages).cuda()
+            kc = inp.k_cache.index_select(0, flat)
+            vc = inp.v_cache.index_select(0, flat)
+            width = max(len(p) for p in pages)
+            table = np.full((nseq, width), -1, np.int32)
+            off = 0
+            for b, p in enumerate(pages):
+                table[b, :len(p)] = np.arange(off, off + len(p))
+                off += len(p)
+            q = inp.q[:nseq]
+            cu = np.arange(nseq + 1, dtype=np.int32)
+            seq = np.asarray([L + 1 for L in case.cache_seqlens[:nseq]], np.int32)
+            qh, kh, vh = wl.host(q), wl.host(kc), wl.host(vc)
+            t0 = time.perf_counter()
+            o, l = oracle.attention(qh, kh, vh, table, seq, cu, dtype="f16", appended=False,
+                                    causal=False, threads=threads)
+            return time.perf_counter() - t0, o, l
+
+        t1, _, _ = sample(1)
+        nseq = int(max(1, min(case.batch, args.cpu_seconds / max(t1, 1e-3))))
+        log(f"bench: oracle on {nseq} sequences ({t1:.2f}s for one)")
+        tc, o_ref, l_ref = sample(nseq)
+        sub = wl.Case(**{**attn_case.__dict__, "q_lens": [1] * nseq,
+                         "cache_seqlens": attn_case.cache_seqlens[:nseq]})
+        cpu_gbs = algorithmic_bytes(sub) / tc / 1e9
+        cpu = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{nseq} of {case.batch} sequences (all 32 heads, {args.ctx + 1} keys "
+                         f"each) of the same decode step, fp64 gather-then-softmax, "
+                         f"{tc:.2f} s"}
+        # sampled full-size parity: the attention-only output of those sequences
+        attn_only()
+        torch.cuda.synchronize()
+        got = out[:nseq].float().cpu().numpy()
+        err = float(np.abs(got - o_ref).max())
+        lerr = float((np.abs(lse[:nseq].cpu().numpy() - l_ref) / np.abs(l_ref)).max())
+        parity = {"rows": nseq * case.num_heads_q, "out_max_abs_err": err,
+                  "lse_max_rel_err": lerr, "ok": bool(err <= 2e-3 and lerr <= 1e-4)}
+
+    # ---- secondary: causal prefill with append ----
+    prefill = None
+    if not args.no_prefill:
+        del inp
+        torch.cuda.empty_cache()
+        pc = wl.causal_prefill_append(2048, "zero")
+        pin = wl.make_inputs(pc, "cuda")
+        pout = torch.empty_like(pin.q)
+        plse = torch.empty(pin.q.shape[0], pin.q.shape[1], dtype=torch.float32, device="cuda")
+
+        def pstep():
+            pa.paged_attn_fwd(pin.q, pin.k_cache, pin.v_cache, pin.block_table, pin.cache_seqlens,
+                              pin.cu_seqlens_q, max_seqlen_q=pin.max_seqlen_q, k_new=pin.k_new,
+                              v_new=pin.v_new, causal=True, out=pout, softmax_lse=plse)
+
+        pms = time_calls(pstep, max(3, args.steps // 2), 2, torch)
+        fl = causal_flops(pc)
+        tfs = fl / (pms * 1e-3) / 1e12
+        prefill = {"workload": pc.name, "ms": round(pms, 4), "tflops": round(tfs, 2),
+                   "peak": MFMA_F16_PEAK_TFS, "frac": round(tfs / MFMA_F16_PEAK_TFS, 4),
+                   "flops_per_call": fl}
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": case.name + "_append1", "batch": case.batch,
+                   "context": args.ctx, "heads_q": 32, "heads_kv": 32, "head_dim": 128,
+                   "page_size": 16, "bytes_per_step": step_bytes, "splits": splits},
+        "roofline": roofline, "cpu_baseline": cpu, "parity_sample": parity, "prefill": prefill,
+        "device": dev.name,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

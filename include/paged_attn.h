@@ -1,0 +1,178 @@
+/*
+ * paged_attn.h - C ABI of the MI355X (gfx950) paged KV-cache attention library
+ * (libpaged_attn.so).
+ *
+ * The operation is the paged KV-cache attention forward pass that the
+ * flash-attention thread "Add support for small page sizes" exercises in its
+ * reproduction script (a block_table maps each sequence's logical pages, 16 to
+ * 256 tokens each, onto a shared physical K/V pool; new K/V rows are appended
+ * at cache_seqlens and then attended to, causally), generalised to the packed
+ * variable-length batches of the vLLM thread "Unify the kernel used in flash
+ * attention backend" (prefill chunks and decode tokens in one call) and to the
+ * MQA/GQA head layouts of the vLLM pull request "Introduce flash-attn
+ * (>= 2.5.0)".
+ *
+ * Conventions shared by every entry point
+ *  - Pure C: no HIP or C++ types cross this boundary.  A stream is passed as
+ *    `void *` holding a hipStream_t (NULL = the legacy default stream).
+ *  - Every device buffer is owned by the caller.  The library never allocates,
+ *    frees or synchronises inside paged_attn_fwd / paged_kv_append (the
+ *    reproduction-script thread notes the call reaches memory only through the
+ *    block table; the determine_num_splits issue rules out reading device
+ *    lengths back to the host).  Scratch space comes in through `workspace`.
+ *  - Launch shape and kernel choice depend only on host-side fields, so a call
+ *    can be captured in a HIP graph; the CUDA-graph comment of the "Unify the
+ *    kernel" thread sets the rule: static maxima, static metadata buffers,
+ *    padded batch slots with zero lengths.
+ *  - Errors the host can see are returned before anything is launched.  A
+ *    launch failure returns PA_ERR_HIP.  Device-side faults are asynchronous
+ *    and surface at the caller's next synchronisation.  No exception crosses
+ *    the ABI.  The library keeps no mutable global state except a per-device
+ *    cache of the compute-unit count.
+ *  - Element types: q, caches, k_new, v_new and out share one 16-bit float
+ *    type (fp16 or bf16).  Accumulation is fp32; out is rounded to nearest
+ *    even once; softmax_lse is fp32, natural log.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  PA_ERR_DTYPE = 3,       /* dtype is not PA_F16 / PA_BF16 */
+  PA_ERR_UNSUPPORTED = 4, /* head_dim or page size this build does not serve */
+  PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than paged_attn_workspace_size */
+  PA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+} pa_status;
+
+typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
+
+/*
+ * Arguments of one forward call.  All sizes are host integers; every pointer
+ * except workspace-less cases must be a device pointer.
+ *
+ * Shapes (row-major, dense):
+ *   q            [total_q, num_heads_q, head_dim]                dtype
+ *   k_cache,     paged:      [num_pages, page_size, num_heads_kv, head_dim]
+ *   v_cache      contiguous: [batch, contig_alloc, num_heads_kv, head_dim]
+ *   block_table  [batch, max_pages_per_seq] int32, or NULL for contiguous mode
+ *   cache_seqlens[batch] int32: tokens already in the cache; NOT modified
+ *   cu_seqlens_q [batch + 1] int32: cu[0] = 0, non-decreasing, cu[batch] =
+ *                total_q; sequence b owns packed rows cu[b] .. cu[b+1]-1
+ *   k_new, v_new [total_q, num_heads_kv, head_dim] dtype, or both NULL
+ *   out          [total_q, num_heads_q, head_dim] dtype (written)
+ *   softmax_lse  [total_q, num_heads_q] float (written)
+ *
+ * Semantics (the plainest reading of the pages, where they are silent):
+ *   - With k_new/v_new, new row i of sequence b is first written to logical
+ *     position cache_seqlens[b] + i (page block_table[b][pos / page_size],
+ *     slot pos % page_size), then attended to: K_b = cache_seqlens[b] + q_len_b.
+ *     Without them K_b = cache_seqlens[b].
+ *   - Causal masking is bottom-right aligned: new token i of sequence b sits at
+ *     position K_b - q_len_b + i and sees keys 0 .. K_b - q_len_b + i.
+ *   - q head h reads kv head h / (num_heads_q / num_heads_kv).
+ *   - A row with no visible key gets out = 0 and softmax_lse = -inf.
+ *   - Sequences with q_len_b = 0 (e.g. padded graph slots) write nothing.
+ *   - Only the first cdiv(K_b, page_size) entries of a table row are read.
+ *
+ * Preconditions the host cannot check (device-resident metadata):
+ *   q_len_b <= max_seqlen_q; K_b <= max_pages_per_seq * page_size (contiguous
+ *   mode: K_b <= contig_alloc); the page ids read lie in [0, num_pages);
+ *   append targets of different sequences are distinct slots; k_new/v_new do
+ *   not alias the caches.  Device code never reads outside the table row or
+ *   the pool: a key whose page id is out of range is treated as absent and an
+ *   append to such a slot is dropped.
+ */
+typedef struct pa_fwd_args {
+  int32_t dtype;             /* pa_dtype */
+  int32_t batch;             /* >= 1 */
+  int32_t total_q;           /* rows of q (host-static upper bound allowed: >= cu[batch]) */
+  int32_t max_seqlen_q;      /* >= every q_len_b (host-static) */
+  int32_t max_seqlen_k;      /* host bound on K_b; 0 -> max_pages_per_seq*page_size (or contig_alloc) */
+  int32_t num_heads_q;
+  int32_t num_heads_kv;      /* num_heads_q % num_heads_kv == 0 */
+  int32_t head_dim;          /* 64 or 128 */
+  int32_t page_size;         /* paged mode: power of two in [16, 256] */
+  int32_t num_pages;         /* paged mode: pool size */
+  int32_t max_pages_per_seq; /* paged mode: block_table width */
+  int32_t contig_alloc;      /* contiguous mode: tokens allocated per sequence */
+  int32_t causal;            /* 0 / 1 */
+  int32_t num_splits;        /* 0 = heuristic; 1..128 = forced split-KV count */
+  float softmax_scale;       /* <= 0 -> 1/sqrt(head_dim) */
+  int32_t reserved0;         /* must be 0 */
+  const void *q;
+  void *k_cache;
+  void *v_cache;
+  const int32_t *block_table;
+  const int32_t *cache_seqlens;
+  const int32_t *cu_seqlens_q;
+  const void *k_new;
+  const void *v_new;
+  void *out;
+  float *softmax_lse;
+  void *workspace;           /* device scratch, caller-owned; may be NULL if size is 0 */
+  size_t workspace_bytes;
+} pa_fwd_args;
+
+/*
+ * paged_attn_fwd - the whole forward call on `stream`: append k_new/v_new into
+ * the pages (if given), attend over each sequence's cache, and - when the
+ * split-KV count is above one - merge the per-split partial results with a
+ * log-sum-exp combine.  Kernels run in that order on the one stream; the call
+ * returns as soon as they are queued.
+ * Returns PA_OK or the first host-detected error (nothing launched then).
+ */
+pa_status paged_attn_fwd(const pa_fwd_args *args, void *stream);
+
+/*
+ * paged_kv_append - the append step alone (vLLM's reshape_and_cache): writes
+ * k_new/v_new rows to positions cache_seqlens[b] + i through the block table
+ * (or the contiguous cache).  Reads only the fields the append needs
+ * (dtype, batch, total_q, max_seqlen_q, num_heads_kv, head_dim, page_size,
+ * num_pages, max_pages_per_seq, contig_alloc, k_cache, v_cache, block_table,
+ * cache_seqlens, cu_seqlens_q, k_new, v_new).  A bit copy: no rounding.
+ */
+pa_status paged_kv_append(const pa_fwd_args *args, void *stream);
+
+/*
+ * paged_attn_workspace_size - bytes of device workspace paged_attn_fwd needs
+ * for these arguments (0 when no split-KV partials are kept).  Host only; no
+ * device access.  Returns 0 for invalid arguments as well.
+ */
+size_t paged_attn_workspace_size(const pa_fwd_args *args);
+
+/*
+ * paged_attn_splits_for - the split-KV count paged_attn_fwd will use for these
+ * arguments (the forced value, or the heuristic on this device), or -1 for
+ * invalid arguments.  Host only apart from one cached device-attribute query.
+ */
+int32_t paged_attn_splits_for(const pa_fwd_args *args);
+
+/*
+ * paged_attn_num_splits - the split-count heuristic (host only, pure function
+ * of its arguments).  The determine_num_splits issue fixes its inputs to
+ * host-known sizes (batch, heads, head size, query and key lengths, compute
+ * unit count) and caps it below 128; lengths on the device are never read.
+ * Returns a value in [1, 128].
+ */
+int32_t paged_attn_num_splits(int32_t batch, int32_t total_q, int32_t num_heads_q,
+                              int32_t num_heads_kv, int32_t head_dim,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t num_cus);
+
+/* paged_attn_status_string - static, human-readable text for a status code. */
+const char *paged_attn_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,242 @@
+"""Python binding of libpaged_attn.so (the MI355X paged KV-cache attention library).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind the C ABI declared in ``include/paged_attn.h``.  PyTorch
+provides device memory (outputs, workspace) and the current stream.  There is
+no fallback: if the shared library is missing and cannot be built, or a call
+fails, an exception is raised.
+
+Functions keep the C names: ``paged_attn_fwd``, ``paged_kv_append``,
+``paged_attn_workspace_size``, ``paged_attn_splits_for``,
+``paged_attn_num_splits``, ``paged_attn_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from . import _build
+
+__all__ = [
+    "PagedAttnError", "paged_attn_fwd", "paged_kv_append", "paged_attn_workspace_size",
+    "paged_attn_splits_for", "paged_attn_num_splits", "paged_attn_status_string", "library_path",
+    "EXPORTED_SYMBOLS",
+]
+
+EXPORTED_SYMBOLS = ("paged_attn_fwd", "paged_kv_append", "paged_attn_workspace_size",
+                    "paged_attn_splits_for", "paged_attn_num_splits", "paged_attn_status_string")
+
+PA_F16, PA_BF16 = 0, 1
+_DTYPE_CODE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({paged_attn_status_string(status)})")
+
+
+class _Args(ctypes.Structure):
+    """Mirror of ``pa_fwd_args``."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32), ("total_q", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+        ("num_heads_q", ctypes.c_int32), ("num_heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32), ("contig_alloc", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("reserved0", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("cache_seqlens", ctypes.c_void_p),
+        ("cu_seqlens_q", ctypes.c_void_p), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("softmax_lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib_handle = None
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        P = ctypes.POINTER(_Args)
+        lib.paged_attn_fwd.restype = ctypes.c_int
+        lib.paged_attn_fwd.argtypes = [P, ctypes.c_void_p]
+        lib.paged_kv_append.restype = ctypes.c_int
+        lib.paged_kv_append.argtypes = [P, ctypes.c_void_p]
+        lib.paged_attn_workspace_size.restype = ctypes.c_size_t
+        lib.paged_attn_workspace_size.argtypes = [P]
+        lib.paged_attn_splits_for.restype = ctypes.c_int32
+        lib.paged_attn_splits_for.argtypes = [P]
+        lib.paged_attn_num_splits.restype = ctypes.c_int32
+        lib.paged_attn_num_splits.argtypes = [ctypes.c_int32] * 8
+        lib.paged_attn_status_string.restype = ctypes.c_char_p
+        lib.paged_attn_status_string.argtypes = [ctypes.c_int32]
+        _lib_handle = lib
+    return _lib_handle
+
+
+def paged_attn_status_string(status: int) -> str:
+    return _lib().paged_attn_status_string(int(status)).decode()
+
+
+def paged_attn_num_splits(batch, total_q, num_heads_q, num_heads_kv, head_dim, max_seqlen_q,
+                          max_seqlen_k, num_cus) -> int:
+    return int(_lib().paged_attn_num_splits(batch, total_q, num_heads_q, num_heads_kv, head_dim,
+                                            max_seqlen_q, max_seqlen_k, num_cus))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(name, t, dtype=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *, max_seqlen_q,
+              max_seqlen_k=0, k_new=None, v_new=None, causal=False, num_splits=0,
+              softmax_scale=None, out=None, softmax_lse=None, workspace=None) -> _Args:
+    """Fill a ``pa_fwd_args`` from tensors (shapes read from the tensors)."""
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError("q must be float16 or bfloat16")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
+                    ("v_new", v_new), ("out", out)):
+        _check_dev(name, t, dt)
+    for name, t in (("block_table", block_table), ("cache_seqlens", cache_seqlens),
+                    ("cu_seqlens_q", cu_seqlens_q)):
+        _check_dev(name, t, torch.int32)
+    _check_dev("softmax_lse", softmax_lse, torch.float32)
+    total_q, hq, d = q.shape
+    a = _Args()
+    a.dtype = _DTYPE_CODE[dt]
+    a.batch = cache_seqlens.shape[0]
+    a.total_q = total_q
+    a.max_seqlen_q = int(max_seqlen_q)
+    a.max_seqlen_k = int(max_seqlen_k)
+    a.num_heads_q = hq
+    a.num_heads_kv = k_cache.shape[2]
+    a.head_dim = d
+    if block_table is not None:
+        a.page_size = k_cache.shape[1]
+        a.num_pages = k_cache.shape[0]
+        a.max_pages_per_seq = block_table.shape[1]
+        a.contig_alloc = 0
+    else:
+        a.contig_alloc = k_cache.shape[1]
+    a.causal = int(bool(causal))
+    a.num_splits = int(num_splits)
+    a.softmax_scale = float(softmax_scale) if softmax_scale is not None else 0.0
+    a.reserved0 = 0
+    a.q = _ptr(q)
+    a.k_cache = _ptr(k_cache)
+    a.v_cache = _ptr(v_cache)
+    a.block_table = _ptr(block_table)
+    a.cache_seqlens = _ptr(cache_seqlens)
+    a.cu_seqlens_q = _ptr(cu_seqlens_q)
+    a.k_new = _ptr(k_new)
+    a.v_new = _ptr(v_new)
+    a.out = _ptr(out)
+    a.softmax_lse = _ptr(softmax_lse)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return a
+
+
+def paged_attn_workspace_size(args: _Args) -> int:
+    return int(_lib().paged_attn_workspace_size(ctypes.byref(args)))
+
+
+def paged_attn_splits_for(args: _Args) -> int:
+    return int(_lib().paged_attn_splits_for(ctypes.byref(args)))
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *,
+                   max_seqlen_q: int, max_seqlen_k: int = 0, k_new=None, v_new=None,
+                   causal: bool = False, num_splits: int = 0, softmax_scale=None, out=None,
+                   softmax_lse=None, workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Paged attention forward (with optional in-call append of k_new/v_new).
+
+    q [total_q, Hq, D]; k_cache/v_cache [num_pages, page_size, Hkv, D] (or
+    [batch, alloc, Hkv, D] with ``block_table=None``); block_table [batch,
+    width] int32; cache_seqlens [batch] int32; cu_seqlens_q [batch+1] int32.
+    ``max_seqlen_q`` must bound every q_len on the host side (no device read).
+    Returns (out [total_q, Hq, D], softmax_lse [total_q, Hq] fp32).
+    """
+    if out is None:
+        out = torch.empty_like(q)
+    if softmax_lse is None:
+        softmax_lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    args = make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q,
+                     max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, k_new=k_new,
+                     v_new=v_new, causal=causal, num_splits=num_splits,
+                     softmax_scale=softmax_scale, out=out, softmax_lse=softmax_lse,
+                     workspace=workspace)
+    if workspace is None:
+        need = paged_attn_workspace_size(args)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            args.workspace = workspace.data_ptr()
+            args.workspace_bytes = need
+    st = _lib().paged_attn_fwd(ctypes.byref(args), ctypes.c_void_p(_stream_handle(stream)))
+    if st != 0:
+        raise PagedAttnError(st, "paged_attn_fwd")
+    return out, softmax_lse
+
+
+def paged_kv_append(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, k_new, v_new, *,
+                    max_seqlen_q: int, stream=None) -> None:
+    """Write k_new/v_new rows at positions cache_seqlens[b] + i (bit copy)."""
+    dt = k_cache.dtype
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
+                    ("v_new", v_new)):
+        _check_dev(name, t, dt)
+    a = _Args()
+    a.dtype = _DTYPE_CODE[dt]
+    a.batch = cache_seqlens.shape[0]
+    a.total_q = k_new.shape[0]
+    a.max_seqlen_q = int(max_seqlen_q)
+    a.num_heads_q = k_new.shape[1]
+    a.num_heads_kv = k_new.shape[1]
+    a.head_dim = k_new.shape[2]
+    if block_table is not None:
+        a.page_size = k_cache.shape[1]
+        a.num_pages = k_cache.shape[0]
+        a.max_pages_per_seq = block_table.shape[1]
+    else:
+        a.contig_alloc = k_cache.shape[1]
+    a.k_cache = _ptr(k_cache)
+    a.v_cache = _ptr(v_cache)
+    a.block_table = _ptr(block_table)
+    a.cache_seqlens = _ptr(cache_seqlens)
+    a.cu_seqlens_q = _ptr(cu_seqlens_q)
+    a.k_new = _ptr(k_new)
+    a.v_new = _ptr(v_new)
+    st = _lib().paged_kv_append(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream)))
+    if st != 0:
+        raise PagedAttnError(st, "paged_kv_append")

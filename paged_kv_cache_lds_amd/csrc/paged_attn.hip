@@ -1,0 +1,281 @@
+// Host dispatch and C ABI of libpaged_attn.so (declarations and contracts in
+// include/paged_attn.h).  Validates arguments, plans the launch from
+// host-static sizes only, carves the caller's workspace and queues
+// append -> attention -> combine on the caller's stream.  Never allocates,
+// frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "paged_attn.h"
+#include "pa_kernels.h"
+
+namespace {
+
+using pa::kThreads;
+
+constexpr int kMaxSplits = 128;
+
+struct Plan {
+  int splits = 1;
+  bool all_decode = true;
+  long grid = 0;          // attention workgroups
+  size_t ws_bytes = 0;
+  size_t o_part_off = 0, lse_part_off = 0;
+  int max_seqlen_k = 0;
+};
+
+inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+inline int ilog2(int x) { int s = 0; while ((1 << s) < x) ++s; return s; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+// Argument checks shared by every entry point.  `append_only` relaxes the
+// fields the append step does not read.
+pa_status validate(const pa_fwd_args *a, bool append_only) {
+  if (a == nullptr) return PA_ERR_NULL;
+  if (a->dtype != PA_F16 && a->dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (a->reserved0 != 0) return PA_ERR_SHAPE;
+  if (a->batch < 1 || a->total_q < 0 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
+    return PA_ERR_SHAPE;
+  if (a->total_q > 0 && a->max_seqlen_q < 1) return PA_ERR_SHAPE;
+  if (a->num_heads_kv < 1) return PA_ERR_SHAPE;
+  if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (a->block_table != nullptr) {
+    if (!is_pow2(a->page_size) || a->page_size < 16 || a->page_size > 256)
+      return PA_ERR_UNSUPPORTED;
+    if (a->num_pages < 1 || a->max_pages_per_seq < 1) return PA_ERR_SHAPE;
+  } else if (a->contig_alloc < 1) {
+    return PA_ERR_SHAPE;
+  }
+  if (a->k_cache == nullptr || a->v_cache == nullptr || a->cache_seqlens == nullptr ||
+      a->cu_seqlens_q == nullptr)
+    return PA_ERR_NULL;
+  if ((a->k_new == nullptr) != (a->v_new == nullptr)) return PA_ERR_NULL;
+  if (append_only) {
+    if (a->k_new == nullptr) return PA_ERR_NULL;
+    return PA_OK;
+  }
+  if (a->num_heads_q < 1 || a->num_heads_q % a->num_heads_kv != 0) return PA_ERR_SHAPE;
+  if (a->causal != 0 && a->causal != 1) return PA_ERR_SHAPE;
+  if (a->num_splits < 0 || a->num_splits > kMaxSplits) return PA_ERR_SHAPE;
+  if (!(a->softmax_scale == a->softmax_scale)) return PA_ERR_SHAPE;   // NaN
+  if (a->q == nullptr || a->out == nullptr || a->softmax_lse == nullptr) return PA_ERR_NULL;
+  return PA_OK;
+}
+
+// Compute units of the current device, queried once per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int key_bound(const pa_fwd_args *a) {
+  if (a->max_seqlen_k > 0) return a->max_seqlen_k;
+  if (a->block_table != nullptr) {
+    const long cap = (long)a->max_pages_per_seq * a->page_size;
+    return cap > INT32_MAX ? INT32_MAX : (int)cap;
+  }
+  return a->contig_alloc;
+}
+
+Plan make_plan(const pa_fwd_args *a, int num_cus) {
+  Plan pl;
+  const int group = a->num_heads_q / a->num_heads_kv;
+  pl.max_seqlen_k = key_bound(a);
+  pl.all_decode = (long)a->max_seqlen_q * group <= pa::kDecodeRows;
+  pl.splits = a->num_splits > 0
+                  ? a->num_splits
+                  : paged_attn_num_splits(a->batch, a->total_q, a->num_heads_q, a->num_heads_kv,
+                                          a->head_dim, a->max_seqlen_q, pl.max_seqlen_k, num_cus);
+  long units_per_head = (long)a->batch * pl.splits;
+  if (!pl.all_decode) units_per_head += cdiv((long)a->total_q * group, pa::kPrefillRows);
+  pl.grid = units_per_head * a->num_heads_kv;
+  if (pl.splits > 1) {
+    const size_t rows = (size_t)a->total_q * a->num_heads_q;
+    pl.o_part_off = 0;
+    pl.lse_part_off = align_up((size_t)pl.splits * rows * a->head_dim * sizeof(float), 256);
+    pl.ws_bytes = align_up(pl.lse_part_off + (size_t)pl.splits * rows * sizeof(float), 256);
+  }
+  return pl;
+}
+
+pa::CacheGeom geom_of(const pa_fwd_args *a) {
+  pa::CacheGeom g;
+  g.table = a->block_table;
+  g.page_shift = a->block_table ? ilog2(a->page_size) : 0;
+  g.mpp = a->max_pages_per_seq;
+  g.num_pages = a->num_pages;
+  g.contig_alloc = a->block_table ? 0 : a->contig_alloc;
+  return g;
+}
+
+pa_status launch_append(const pa_fwd_args *a, hipStream_t stream) {
+  if (a->total_q == 0 || a->max_seqlen_q == 0) return PA_OK;
+  pa::AppendParams p;
+  p.k_cache = static_cast<uint16_t *>(a->k_cache);
+  p.v_cache = static_cast<uint16_t *>(a->v_cache);
+  p.geom = geom_of(a);
+  p.cache_seqlens = a->cache_seqlens;
+  p.cu_seqlens_q = a->cu_seqlens_q;
+  p.k_new = static_cast<const uint16_t *>(a->k_new);
+  p.v_new = static_cast<const uint16_t *>(a->v_new);
+  p.batch = a->batch;
+  p.total_q = a->total_q;
+  p.hkv = a->num_heads_kv;
+  p.head_dim = a->head_dim;
+  const int vec_per_row = a->num_heads_kv * a->head_dim / 8;
+  p.tokens_per_block = std::max(1, 1024 / (2 * vec_per_row));
+  dim3 grid((unsigned)cdiv(a->max_seqlen_q, p.tokens_per_block), (unsigned)a->batch);
+  if (grid.y > 65535u) return PA_ERR_SHAPE;
+  hipLaunchKernelGGL(pa::kv_append_kernel, grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+template <int DT, int D>
+pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t stream) {
+  const int group = a->num_heads_q / a->num_heads_kv;
+  pa::FwdParams p;
+  p.q = static_cast<const uint16_t *>(a->q);
+  p.k_cache = static_cast<const uint16_t *>(a->k_cache);
+  p.v_cache = static_cast<const uint16_t *>(a->v_cache);
+  p.geom = geom_of(a);
+  p.cache_seqlens = a->cache_seqlens;
+  p.cu_seqlens_q = a->cu_seqlens_q;
+  p.out = static_cast<uint16_t *>(a->out);
+  p.lse = a->softmax_lse;
+  char *ws = static_cast<char *>(a->workspace);
+  p.o_part = pl.splits > 1 ? reinterpret_cast<float *>(ws + pl.o_part_off) : nullptr;
+  p.lse_part = pl.splits > 1 ? reinterpret_cast<float *>(ws + pl.lse_part_off) : nullptr;
+  p.batch = a->batch;
+  p.total_q = a->total_q;
+  p.hq = a->num_heads_q;
+  p.hkv = a->num_heads_kv;
+  p.group = group;
+  p.appended = a->k_new != nullptr;
+  p.causal = a->causal;
+  p.num_splits = pl.splits;
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale
+                                             : 1.0f / std::sqrt((float)a->head_dim);
+  p.scale_log2 = scale * pa::kLog2e;
+  p.all_decode = pl.all_decode;
+  if (pl.grid > 0x7fffffffL) return PA_ERR_SHAPE;
+  hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(kThreads), 0,
+                     stream, p);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  if (pl.splits > 1) {
+    pa::CombineParams c;
+    c.o_part = p.o_part;
+    c.lse_part = p.lse_part;
+    c.cu_seqlens_q = a->cu_seqlens_q;
+    c.out = p.out;
+    c.lse = p.lse;
+    c.batch = a->batch;
+    c.total_q = a->total_q;
+    c.hq = a->num_heads_q;
+    c.group = group;
+    c.num_splits = pl.splits;
+    c.all_decode = pl.all_decode;
+    const long rows = (long)a->total_q * a->num_heads_q;
+    const long blocks = cdiv(rows, pa::kWaves);
+    if (blocks > 0x7fffffffL) return PA_ERR_SHAPE;
+    hipLaunchKernelGGL((pa::combine_kernel<DT, D>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, c);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paged_attn_num_splits(int32_t batch, int32_t total_q, int32_t num_heads_q,
+                              int32_t num_heads_kv, int32_t head_dim, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, int32_t num_cus) {
+  // Host-only cost model (no device length is read).  Work units without any
+  // split: one per (sequence, kv head) plus the prefill tiles.  If they cover
+  // the machine twice over (two resident 4-wave workgroups per compute unit)
+  // splitting only adds partial-result traffic.  Otherwise split each key
+  // range so the units reach that count, but keep at least 8 key tiles of
+  // 32 per split (two per wave) so a split's fixed cost stays amortised, and
+  // stay within the cap of 128.
+  (void)head_dim;
+  if (batch < 1 || num_heads_q < 1 || num_heads_kv < 1 || max_seqlen_k < 1) return 1;
+  if (num_cus < 1) num_cus = 256;
+  const long group = num_heads_q / num_heads_kv > 0 ? num_heads_q / num_heads_kv : 1;
+  long units = (long)batch * num_heads_kv;
+  if ((long)max_seqlen_q * group > pa::kDecodeRows && total_q > 0)
+    units += cdiv((long)total_q * group, pa::kPrefillRows) * num_heads_kv;
+  const long target = 2L * num_cus;
+  if (units >= target) return 1;
+  long s = cdiv(target, units);
+  const long tiles = cdiv(max_seqlen_k, pa::kKeyTile);
+  const long cap = std::max(1L, tiles / 8);
+  s = std::min(s, cap);
+  s = std::max(1L, std::min(s, (long)kMaxSplits));
+  return (int32_t)s;
+}
+
+int32_t paged_attn_splits_for(const pa_fwd_args *args) {
+  if (validate(args, false) != PA_OK) return -1;
+  return make_plan(args, device_cus()).splits;
+}
+
+size_t paged_attn_workspace_size(const pa_fwd_args *args) {
+  if (validate(args, false) != PA_OK) return 0;
+  return make_plan(args, device_cus()).ws_bytes;
+}
+
+pa_status paged_kv_append(const pa_fwd_args *args, void *stream) {
+  const pa_status st = validate(args, true);
+  if (st != PA_OK) return st;
+  return launch_append(args, static_cast<hipStream_t>(stream));
+}
+
+pa_status paged_attn_fwd(const pa_fwd_args *args, void *stream) {
+  pa_status st = validate(args, false);
+  if (st != PA_OK) return st;
+  if (args->total_q == 0) return PA_OK;
+  const Plan pl = make_plan(args, device_cus());
+  if (pl.ws_bytes > 0 && (args->workspace == nullptr || args->workspace_bytes < pl.ws_bytes))
+    return PA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (args->k_new != nullptr) {
+    st = launch_append(args, s);
+    if (st != PA_OK) return st;
+  }
+  const bool bf16 = args->dtype == PA_BF16;
+  if (args->head_dim == 128)
+    return bf16 ? launch_attention<pa::kBF16, 128>(args, pl, s)
+                : launch_attention<pa::kF16, 128>(args, pl, s);
+  return bf16 ? launch_attention<pa::kBF16, 64>(args, pl, s)
+              : launch_attention<pa::kF16, 64>(args, pl, s);
+}
+
+const char *paged_attn_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "sizes are inconsistent or out of range";
+    case PA_ERR_DTYPE: return "dtype must be PA_F16 or PA_BF16";
+    case PA_ERR_UNSUPPORTED: return "head_dim or page size not supported (head_dim 64/128, page size a power of two in [16, 256])";
+    case PA_ERR_WORKSPACE: return "workspace missing or smaller than paged_attn_workspace_size";
+    case PA_ERR_HIP: return "a HIP launch or runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

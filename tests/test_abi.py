@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, the ctypes mirror matches the C struct layout, host-side
+validation returns the documented status codes without launching anything,
+and the split heuristic has its documented properties."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import paged_kv_cache_lds_amd as pa
+from paged_kv_cache_lds_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:paged_attn|paged_kv)_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pa.library_path() if os.path.exists(pa.library_path()) else _build.build())
+    names = declared_functions()
+    assert set(names) == set(pa.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    for n in names:
+        assert re.search(r"\bT " + n + r"\b", out), n
+
+
+def test_ctypes_struct_matches_c_layout():
+    fields = [f[0] for f in pa._Args._fields_]
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "paged_attn.h"', "int main(void){",
+           'printf("%zu\\n", sizeof(pa_fwd_args));']
+    for f in fields:
+        src.append(f'printf("%zu\\n", offsetof(pa_fwd_args, {f}));')
+    src.append("return 0;}")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write("\n".join(src))
+        exe = os.path.join(d, "t")
+        subprocess.check_call(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe])
+        vals = [int(x) for x in subprocess.check_output([exe]).split()]
+    assert vals[0] == ctypes.sizeof(pa._Args)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(pa._Args, f).offset == off, f
+
+
+def valid_args(**over):
+    a = pa._Args()
+    a.dtype, a.batch, a.total_q, a.max_seqlen_q = 0, 2, 2, 1
+    a.num_heads_q, a.num_heads_kv, a.head_dim = 4, 4, 64
+    a.page_size, a.num_pages, a.max_pages_per_seq = 16, 32, 7
+    a.causal, a.num_splits, a.softmax_scale = 0, 0, 0.0
+    fake = 0x1000
+    for f in ("q", "k_cache", "v_cache", "block_table", "cache_seqlens", "cu_seqlens_q", "out",
+              "softmax_lse"):
+        setattr(a, f, fake)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def call_fwd(a):
+    return pa._lib().paged_attn_fwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(softmax_lse=None), 1), (dict(cu_seqlens_q=None), 1),
+    (dict(k_new=0x1000), 1),                       # k_new without v_new
+    (dict(dtype=7), 3),
+    (dict(head_dim=96), 4), (dict(page_size=24), 4), (dict(page_size=8), 4), (dict(page_size=512), 4),
+    (dict(num_heads_q=6), 2), (dict(num_splits=129), 2), (dict(num_splits=-1), 2),
+    (dict(batch=0), 2), (dict(causal=2), 2), (dict(reserved0=1), 2),
+    (dict(block_table=None, contig_alloc=0), 2),
+    (dict(num_splits=4), 5),                       # splits need a workspace
+])
+def test_host_validation_codes(over, code):
+    assert call_fwd(valid_args(**over)) == code
+
+
+def test_null_args_pointer():
+    assert pa._lib().paged_attn_fwd(None, None) == 1
+    assert pa._lib().paged_kv_append(None, None) == 1
+
+
+def test_workspace_size_and_splits_for_are_host_only():
+    a = valid_args(num_splits=4)
+    need = pa.paged_attn_workspace_size(a)
+    # S * total_q * Hq * (D + 1) fp32, each part padded to 256 bytes
+    assert need >= 4 * 2 * 4 * 65 * 4
+    assert pa.paged_attn_splits_for(a) == 4
+    a.workspace, a.workspace_bytes = 0x2000, need - 1
+    assert call_fwd(a) == 5
+    assert pa.paged_attn_workspace_size(valid_args(num_splits=1)) == 0
+    assert pa.paged_attn_splits_for(valid_args(head_dim=96)) == -1
+
+
+def test_status_strings():
+    for code in range(7):
+        assert pa.paged_attn_status_string(code) != "unknown status"
+    assert pa.paged_attn_status_string(99) == "unknown status"
+
+
+def test_split_heuristic_properties():
+    ns = pa.paged_attn_num_splits
+    # the machine is already full -> no split
+    assert ns(256, 256, 32, 32, 128, 1, 4096, 256) == 1
+    # long-context GQA decode with few sequences -> splits
+    s = ns(8, 8, 64, 8, 128, 1, 131072, 256)
+    assert 2 <= s <= 128
+    # never more splits than 8-tile chunks of the key bound, never above 128
+    assert ns(1, 1, 1, 1, 128, 1, 32 * 8 * 3, 256) <= 3
+    for b in (1, 2, 4, 8, 16, 64):
+        for k in (1, 100, 4096, 131072, 2**31 - 1):
+            v = ns(b, b, 8, 1, 128, 1, k, 256)
+            assert 1 <= v <= 128
+    # more work units never ask for more splits
+    prev = 129
+    for b in range(1, 600, 7):
+        v = ns(b, b, 32, 32, 128, 1, 65536, 256)
+        assert v <= prev
+        prev = v
+    # depends only on its arguments (pure, host-known sizes)
+    assert ns(8, 8, 64, 8, 128, 1, 131072, 256) == ns(8, 8, 64, 8, 128, 1, 131072, 256)
+    # degenerate inputs
+    assert ns(0, 0, 1, 1, 64, 1, 10, 256) == 1
+    assert ns(4, 4, 4, 4, 64, 1, 0, 256) == 1
