@@ -80,6 +80,158 @@ def time_calls(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps     # ms per call
 
 
+def median_call_ms(fn, reps, torch, flush=None):
+    """Median time of single calls, each bracketed by events on the current
+    stream, with `flush` (a 1 GiB HBM read that evicts L2 and the 256 MiB
+    Infinity Cache) run between calls outside the timed region."""
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
+    return times[len(times) // 2], times[0]
+
+
+def sweep(name, reps, out_path):
+    """Measurement sweeps over the workload families (one JSON object per
+    point, appended to `out_path`); each point reports median / min call time
+    and the fraction of its roofline."""
+    import torch
+
+    import paged_kv_cache_lds_amd as pa
+    import workloads as wl
+
+    torch.cuda.set_device(0)
+    # cache flush between timed calls: stream-read 1 GiB (evicts L2 and the
+    # 256 MiB Infinity Cache with clean lines, so no write-back lands in the
+    # next timed call)
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush = lambda: scratch.sum()
+    fh = open(out_path, "a")
+
+    def emit(rec):
+        fh.write(json.dumps(rec) + "\n")
+        fh.flush()
+        print(json.dumps(rec), file=sys.stderr, flush=True)
+
+    def run(case, inp, num_splits=None, max_seqlen_k=None, seqlens=None, append=None):
+        kn = inp.k_new if (append if append is not None else case.append) else None
+        vn = inp.v_new if kn is not None else None
+        seq = inp.cache_seqlens if seqlens is None else seqlens
+        out = torch.empty_like(inp.q)
+        lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device="cuda")
+        args = pa.make_args(inp.q, inp.k_cache, inp.v_cache, inp.block_table, seq,
+                            inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q,
+                            max_seqlen_k=max_seqlen_k if max_seqlen_k is not None else inp.max_seqlen_k,
+                            k_new=kn, v_new=vn, causal=case.causal,
+                            num_splits=case.num_splits if num_splits is None else num_splits,
+                            out=out, softmax_lse=lse)
+        S = pa.paged_attn_splits_for(args)
+        ws = torch.empty(max(1, pa.paged_attn_workspace_size(args)), dtype=torch.uint8, device="cuda")
+
+        def call():
+            pa.paged_attn_fwd(inp.q, inp.k_cache, inp.v_cache, inp.block_table, seq,
+                              inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q,
+                              max_seqlen_k=args.max_seqlen_k, k_new=kn, v_new=vn,
+                              causal=case.causal, num_splits=args.num_splits, out=out,
+                              softmax_lse=lse, workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        med, mn = median_call_ms(call, reps, torch, flush)
+        return S, med, mn
+
+    if name == "copy":
+        n = 1 << 31   # 4 GiB of fp16 read + written
+        a = torch.empty(n, dtype=torch.float16, device="cuda")
+        b = torch.empty_like(a)
+        med, mn = median_call_ms(lambda: b.copy_(a), reps, torch, flush)
+        emit({"sweep": "copy", "bytes": 4 * n, "ms": med, "GBps": 4 * n / med / 1e6})
+    elif name == "decode":
+        # MHA decode, 32 x 128 fp16: one pool per page size reused for every
+        # (batch, context) point through the leading table rows
+        for P in (16, 256):
+            big = wl.mha_decode(256, 4096, page_size=P)
+            inp = wl.make_inputs(big, "cuda")
+            for ctx in (512, 1024, 2048, 4096):
+                for B in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+                    c = wl.mha_decode(B, ctx, page_size=P)
+                    c.causal = False
+                    sub = wl.Inputs(case=c, q=inp.q[:B].contiguous(), k_cache=inp.k_cache,
+                                    v_cache=inp.v_cache,
+                                    block_table=inp.block_table[:B].contiguous(),
+                                    cache_seqlens=torch.full((B,), ctx, dtype=torch.int32,
+                                                             device="cuda"),
+                                    cu_seqlens_q=inp.cu_seqlens_q[:B + 1].contiguous(),
+                                    k_new=None, v_new=None, max_seqlen_q=1, max_seqlen_k=ctx,
+                                    pages_of=[])
+                    S, med, mn = run(c, sub)
+                    by = algorithmic_bytes(c)
+                    emit({"sweep": "decode", "P": P, "batch": B, "ctx": ctx, "splits": S,
+                          "ms": med, "ms_min": mn, "GBps": by / med / 1e6,
+                          "frac": by / med / 1e6 / HBM_PEAK_GBS})
+            del inp
+            torch.cuda.empty_cache()
+    elif name == "gqa":
+        for paged in (True, False):
+            c = wl.gqa_long_split(paged=paged)
+            inp = wl.make_inputs(c, "cuda")
+            by = algorithmic_bytes(c)
+            for hint in ("alloc", "max"):
+                mk = 131072 if hint == "alloc" else max(c.cache_seqlens)
+                S, med, mn = run(c, inp, num_splits=0, max_seqlen_k=mk)
+                emit({"sweep": "gqa", "paged": paged, "splits": S, "heuristic": hint,
+                      "ms": med, "ms_min": mn, "GBps": by / med / 1e6,
+                      "frac": by / med / 1e6 / HBM_PEAK_GBS})
+            for s in (1, 2, 4, 8, 16, 32, 64, 128):
+                S, med, mn = run(c, inp, num_splits=s)
+                emit({"sweep": "gqa", "paged": paged, "splits": S, "heuristic": None,
+                      "ms": med, "ms_min": mn, "GBps": by / med / 1e6,
+                      "frac": by / med / 1e6 / HBM_PEAK_GBS})
+            del inp
+            torch.cuda.empty_cache()
+    elif name == "prefill":
+        for nq, prefix in ((170, "zero"), (170, "uniform"), (2048, "zero"), (2048, "uniform"),
+                           (8192, "zero")):
+            c = wl.causal_prefill_append(nq, prefix)
+            inp = wl.make_inputs(c, "cuda")
+            S, med, mn = run(c, inp)
+            fl = causal_flops(c)
+            emit({"sweep": "prefill", "nq": nq, "prefix": prefix, "ms": med, "ms_min": mn,
+                  "TFLOPs": fl / med / 1e9, "frac": fl / med / 1e9 / MFMA_F16_PEAK_TFS})
+            del inp
+            torch.cuda.empty_cache()
+    elif name == "unified":
+        for heads, hd in ((32, 128), (12, 64)):
+            for nq in (100, 500, 1000):
+                c = wl.unified_varlen(nq, heads=heads, head_dim=hd)
+                inp = wl.make_inputs(c, "cuda")
+                S, med, mn = run(c, inp)
+                by, fl = algorithmic_bytes(c), causal_flops(c)
+                t_roof = max(by / (HBM_PEAK_GBS * 1e9), fl / (MFMA_F16_PEAK_TFS * 1e12)) * 1e3
+                # the same work as two calls: decode rows, then the prefill chunk
+                dec = wl.Case(**{**c.__dict__, "q_lens": c.q_lens[1:],
+                                 "cache_seqlens": c.cache_seqlens[1:]})
+                pre = wl.Case(**{**c.__dict__, "q_lens": c.q_lens[:1],
+                                 "cache_seqlens": c.cache_seqlens[:1]})
+                di = wl.make_inputs(dec, "cuda")
+                pi = wl.make_inputs(pre, "cuda")
+                _, dmed, _ = run(dec, di)
+                _, pmed, _ = run(pre, pi)
+                emit({"sweep": "unified", "nq": nq, "heads": heads, "head_dim": hd, "splits": S,
+                      "ms": med, "ms_min": mn, "roofline_ms": t_roof, "frac": t_roof / med,
+                      "two_call_ms": dmed + pmed})
+                del inp, di, pi
+                torch.cuda.empty_cache()
+    fh.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,7 +243,14 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--sweep", choices=["copy", "decode", "gqa", "prefill", "unified"],
+                    help="run a measurement sweep instead of the headline line")
+    ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
+    ap.add_argument("--reps", type=int, default=10)
     args = ap.parse_args()
+    if args.sweep:
+        sweep(args.sweep, args.reps, args.sweep_out)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence / kv head / key range, see the design notes).",

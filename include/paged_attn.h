@@ -48,7 +48,9 @@ typedef enum pa_status {
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
   PA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
   PA_ERR_DTYPE = 3,       /* dtype is not PA_F16 / PA_BF16 */
-  PA_ERR_UNSUPPORTED = 4, /* head_dim or page size this build does not serve */
+  PA_ERR_UNSUPPORTED = 4, /* head_dim or page size this build does not serve, or one
+                             page (contiguous mode: one sequence's allocation) spans
+                             2 GiB or more */
   PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than paged_attn_workspace_size */
   PA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
 } pa_status;
@@ -145,14 +147,17 @@ pa_status paged_kv_append(const pa_fwd_args *args, void *stream);
 /*
  * paged_attn_workspace_size - bytes of device workspace paged_attn_fwd needs
  * for these arguments (0 when no split-KV partials are kept).  Host only; no
- * device access.  Returns 0 for invalid arguments as well.
+ * device access.  Only sizes and flags are read (data pointers may still be
+ * NULL; k_new/v_new only matter through being NULL or not).  Returns 0 for
+ * invalid sizes as well.
  */
 size_t paged_attn_workspace_size(const pa_fwd_args *args);
 
 /*
  * paged_attn_splits_for - the split-KV count paged_attn_fwd will use for these
  * arguments (the forced value, or the heuristic on this device), or -1 for
- * invalid arguments.  Host only apart from one cached device-attribute query.
+ * invalid sizes.  Reads sizes and flags only, like paged_attn_workspace_size;
+ * host only apart from one cached device-attribute query.
  */
 int32_t paged_attn_splits_for(const pa_fwd_args *args);
 

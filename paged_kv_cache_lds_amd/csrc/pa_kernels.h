@@ -1,9 +1,10 @@
 // gfx950 kernels of the paged KV-cache attention forward pass.
 //
 //   kv_append_kernel   new K/V rows -> their page slots (bit copy)
-//   attn_fwd_kernel    one unified varlen kernel: decode rows and prefill tiles
-//                      in one grid; QK^T and PV on MFMA with fp32 accumulation,
-//                      online softmax, split-KV partial or final epilogue
+//   attn_fwd_kernel    one unified varlen kernel: decode units and prefill
+//                      tiles in one grid; QK^T and PV on MFMA with fp32
+//                      accumulation, online softmax, split-KV partial or final
+//                      epilogue
 //   combine_kernel     log-sum-exp merge of split-KV partials
 #pragma once
 
@@ -12,11 +13,14 @@
 namespace pa {
 
 // Work decomposition constants.
-constexpr int kThreads = 256;   // four wave64 per workgroup
+constexpr int kThreads = 256;     // four wave64 per workgroup
 constexpr int kWaves = 4;
-constexpr int kKeyTile = 32;    // keys per wave main-loop iteration (two 16-key MFMA blocks)
-constexpr int kDecodeRows = 16; // packed (token, q-head) rows of a decode work unit
-constexpr int kPrefillRows = 64;// rows of a prefill work unit: 16 per wave
+constexpr int kKeyTile = 32;      // decode: keys per wave main-loop iteration
+constexpr int kDecodeRows = 16;   // packed (token, q-head) rows of a decode unit
+constexpr int kPrefillRows = 128; // rows of a prefill unit: 32 per wave
+constexpr int kPTile = 64;        // prefill: keys per workgroup main-loop iteration
+constexpr int kMaxSplits = 128;
+constexpr int kWindow = 64;       // block-table entries a wave holds at once (one per lane)
 
 struct FwdParams {
   const uint16_t *q;
@@ -27,12 +31,13 @@ struct FwdParams {
   const int32_t *cu_seqlens_q;
   uint16_t *out;
   float *lse;
-  float *o_part;     // [S, total_q, hq, D] fp32 (S > 1)
-  float *lse_part;   // [S, total_q, hq]
+  float *o_part;       // [max_splits, total_q, hq, D] fp32 (num_splits > 1)
+  float *lse_part;     // [max_splits, total_q, hq]
+  int32_t *split_count;// [batch]: splits given to each decode-mode sequence
   int batch, total_q, hq, hkv, group;
   int appended, causal, num_splits;
-  float scale_log2;  // softmax scale * log2(e)
-  int all_decode;    // host knows every sequence has q_len * group <= 16
+  float scale_log2;    // softmax scale * log2(e)
+  int all_decode;      // host knows every sequence has q_len * group <= 16
 };
 
 struct AppendParams {
@@ -83,185 +88,310 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Unified work mapping.  Work units per kv head: a sequence whose packed rows
-// (q_len * group) fit one 16-row decode unit gets num_splits units (its keys
-// split across workgroups); a longer one gets cdiv(rows, 64) prefill units of
-// one split each.  The host sizes the grid from static maxima only; each
-// workgroup finds its (sequence, unit) by a block-wide scan of the device
-// cu_seqlens_q, and surplus workgroups return at once.  Zero-length
-// sequences own no unit.
+// Per-sequence bookkeeping shared by every workgroup (and by the combine).
 // ---------------------------------------------------------------------------
-__device__ inline int units_of_sequence(int rows, int num_splits) {
-  if (rows <= 0) return 0;
-  return rows <= kDecodeRows ? num_splits : (rows + kPrefillRows - 1) / kPrefillRows;
+struct SeqInfo {
+  int cu_b, q_len, K_b;
+};
+
+__device__ inline SeqInfo seq_info(const FwdParams &p, int b) {
+  SeqInfo s;
+  s.cu_b = p.cu_seqlens_q[b];
+  s.q_len = max(0, min(p.cu_seqlens_q[b + 1], p.total_q) - s.cu_b);
+  s.K_b = max(0, p.cache_seqlens[b]) + (p.appended ? s.q_len : 0);
+  return s;
 }
 
-__device__ inline bool locate_unit(const FwdParams &p, int unit, int &b_out, int &off_out,
-                                   int *s_wsum, int *s_found) {
+// Splits of a decode-mode sequence.  The host fixes the unit budget per kv
+// head (num_splits per decode sequence on average) from static sizes only;
+// here, with the real lengths in hand, every decode sequence keeps one unit
+// and the remaining budget is shared in proportion to its key tiles, so long
+// sequences get more splits than short ones (cache_seqlens never travels to
+// the host).  A pure function of the lengths: every workgroup agrees on it.
+__device__ inline int seq_splits(long extra_budget, long tiles_b, long total_tiles) {
+  if (extra_budget <= 0 || total_tiles <= 0) return 1;
+  const long s = 1 + (extra_budget * tiles_b) / total_tiles;
+  return (int)min(s, (long)kMaxSplits);
+}
+
+__device__ inline int decode_tiles(int K_b) { return (K_b + kKeyTile - 1) / kKeyTile; }
+
+// inclusive prefix sum over the workgroup (every thread contributes x);
+// `total` receives the workgroup sum
+__device__ inline int block_inclusive_scan(int x, int *s_wsum, int &total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wsum[wave] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int v = s_wsum[w];
+    before += (w < wave) ? v : 0;
+    total += v;
+  }
+  __syncthreads();
+  return before + x;
+}
+
+// Unified work mapping.  Units per kv head: a sequence whose packed rows
+// (q_len * group) fit one 16-row decode unit gets seq_splits() units (its
+// keys split across workgroups); a longer one gets cdiv(rows, 128) prefill
+// units, heaviest (last, under the causal mask) first.  The host sizes the
+// grid from static maxima; each workgroup finds its (sequence, unit) by
+// block-wide scans over the device metadata, and surplus workgroups return.
+struct UnitInfo {
+  int b, off, splits;   // off = split (decode) or query tile (prefill)
+};
+
+__device__ inline bool locate_unit(const FwdParams &p, int unit, UnitInfo &u, int *s_wsum,
+                                   int *s_found) {
+  const int tid = threadIdx.x;
+  const int S = p.num_splits;
+  // pass 1: decode-mode sequence count and their key tiles
+  long extra = 0, total_tiles = 0;
+  if (S > 1) {
+    long n_dec = 0, tiles = 0;
+    for (int c0 = 0; c0 < p.batch; c0 += kThreads) {
+      const int bb = c0 + tid;
+      int dec = 0, t = 0;
+      if (bb < p.batch) {
+        const SeqInfo si = seq_info(p, bb);
+        const int rows = si.q_len * p.group;
+        if (rows > 0 && (p.all_decode || rows <= kDecodeRows)) {
+          dec = 1;
+          t = decode_tiles(si.K_b);
+        }
+      }
+      int tot_d, tot_t;
+      block_inclusive_scan(dec, s_wsum, tot_d);
+      block_inclusive_scan(t, s_wsum, tot_t);
+      n_dec += tot_d;
+      tiles += tot_t;
+    }
+    extra = n_dec * (S - 1);
+    total_tiles = tiles;
+  }
+  // pass 2: prefix of units, find ours
   if (tid == 0) s_found[0] = -1;
   __syncthreads();
   int carry = 0;
   for (int c0 = 0; c0 < p.batch; c0 += kThreads) {
     const int bb = c0 + tid;
-    int units = 0;
+    int units = 0, splits = 1;
     if (bb < p.batch) {
-      const int ql = p.cu_seqlens_q[bb + 1] - p.cu_seqlens_q[bb];
-      units = units_of_sequence(ql * p.group, p.num_splits);
+      const SeqInfo si = seq_info(p, bb);
+      const int rows = si.q_len * p.group;
+      if (rows > 0) {
+        if (p.all_decode || rows <= kDecodeRows) {
+          splits = seq_splits(extra, decode_tiles(si.K_b), total_tiles);
+          units = splits;
+        } else {
+          units = (rows + kPrefillRows - 1) / kPrefillRows;
+        }
+      }
     }
-    int x = units;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) s_wsum[wave] = x;
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const int v = s_wsum[w];
-      before += (w < wave) ? v : 0;
-      total += v;
-    }
-    const int incl = carry + before + x;
+    int total;
+    const int incl = carry + block_inclusive_scan(units, s_wsum, total);
     const int excl = incl - units;
     if (units > 0 && unit >= excl && unit < incl) {
       s_found[0] = bb;
       s_found[1] = unit - excl;
+      s_found[2] = splits;
     }
     carry += total;
     __syncthreads();
     if (s_found[0] >= 0) break;
   }
-  b_out = s_found[0];
-  off_out = s_found[1];
-  return b_out >= 0;
+  u.b = s_found[0];
+  u.off = s_found[1];
+  u.splits = s_found[2];
+  return u.b >= 0;
+}
+
+// keys visible to packed row r of a sequence (bottom-right causal alignment)
+__device__ inline int row_key_bound(int r, int group, int q_len, int K_b, int causal) {
+  if (!causal) return K_b;
+  const int lim = K_b - q_len + r / group + 1;
+  return max(0, min(lim, K_b));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer loads over one page (or one contiguous sequence) of the pool:
+// 32-bit per-lane byte offsets against a wave-uniform base, and any offset at
+// or past the range returns zeros without touching memory.  Masked lanes use
+// kOOB, so no load sits behind a branch and the compiler can count
+// outstanding loads exactly (keeping several tiles in flight).
+constexpr uint32_t kOOB = 0x80000000u;
+__device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+// Streaming variant (nt: the rows are read once and should not displace
+// cached data): lane offset plus a wave-uniform offset.
+__device__ inline u32x4 buf_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t lane_off,
+                                          uint32_t uniform_off) {
+  return __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, (int)uniform_off, 2));
+}
+
+// Geometry of one "slab" the buffer loads address: a physical page in paged
+// mode, a sequence's whole allocation in contiguous mode.  A key's row within
+// the slab is key % page_size (paged) or key (contiguous).
+struct Slab {
+  uint32_t bytes;        // bytes per slab (host checks < 2^31)
+  long elems;            // halves per slab
+};
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i % 4 of the 8-byte rows addressed by lanes i / 4 + 4 j,
+// j = 0..3.  Lane s addressing row k0 + s / 4, columns c0 + 4 (s % 4) .. +3 of
+// a row-major [key][dim] tile therefore hands lane i the four keys k0 .. k0+3
+// of dim c0 + i: the key-contiguous operand layout the PV product needs.
+__device__ inline u32x2 lds_read_tr16(const uint16_t *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // ---------------------------------------------------------------------------
-// Unified attention kernel.
+// Decode unit: <= 16 packed rows (the G q heads of one kv head for one or a
+// few tokens), one split of the sequence's keys.  The four waves share the
+// rows and each walks a contiguous quarter of the split's 32-key tiles:
 //
-// One workgroup = one work unit (sequence b, kv head g, query tile, key
-// split).  Each wave owns 16 packed query rows (row r = token r / group,
-// q head g * group + r % group: the group's q heads share every K/V fetch)
-// and runs the main loop over 32-key tiles:
-//
-//   page gather   every lane resolves the physical page of its own key from
-//                 the block table by absolute index, once per tile, and loads
-//                 16-byte K and V vectors straight from HBM (the next tile's
-//                 loads are issued before the current tile is computed);
-//   S^T = K Q^T   v_mfma_f32_16x16x32 with keys on M and query rows on N, so
-//                 the softmax probabilities come out already in the layout
-//                 the PV product takes as its B operand;
-//   softmax       online: running max in log2 units (scale * log2 e folded
-//                 into one multiply), rescale of the accumulator, per-lane
-//                 partial row sums reduced once at the end;
-//   O^T += V^T P^T v_mfma_f32_16x16x32, V transposed through the wave's own
-//                 LDS region (no workgroup barrier in the loop).
-//
-// Decode units (<= 16 rows): the four waves share the rows and interleave the
-// unit's key tiles; their states merge through LDS.  Prefill units (64 rows):
-// each wave has its own 16 rows and walks every key tile its rows can see.
-// Key tiles are 32 keys whatever the page size, so results do not depend on
-// the page size or on which physical pages hold the keys.
+//   page window  each lane holds the physical id of one of the next 64
+//                logical pages (one table load per 64 pages); the one or two
+//                pages a tile touches are read out of the window with scalar
+//                lane reads, so no table access sits between tiles; ids are
+//                resolved by absolute logical index, and entries past the
+//                last visible page are never read;
+//   row loads    every load instruction fetches whole K (V) rows: D*2 bytes
+//                per key, 64*16/(D*2) keys per instruction, which streams
+//                HBM faster than MFMA-shaped partial-row loads; two tiles are
+//                in flight per wave (tile t + 2 is issued as soon as tile t's
+//                registers are staged);
+//   LDS staging  K and V land in the wave's own LDS region, rows with their
+//                16-byte chunks XOR-swizzled by key, so both the MFMA-layout
+//                K reads and the transposing V reads are bank-conflict free;
+//                no workgroup barrier in the loop;
+//   S^T = K Q^T  16x16x32 MFMA, keys on M: each lane's probabilities are
+//                already the B operand of the PV product;
+//   O^T += V^T P^T 16x16x32 MFMA on key-contiguous V^T from transposing reads.
+// The waves' (max, sum, O) states merge through LDS at the end.
 // ---------------------------------------------------------------------------
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
+__device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, const int g,
+                                            const int split, const int S_b, const SeqInfo si,
+                                            uint16_t *smem, float (*sm_m)[kDecodeRows],
+                                            float (*sm_l)[kDecodeRows]) {
   constexpr int DS = D / 32;       // k-steps of S^T (32 dims each)
   constexpr int DB = D / 16;       // 16-dim blocks of O^T
-  constexpr int VSTR = D + 8;      // padded LDS row (halves) of the V tile
-  constexpr int REGION = kKeyTile * VSTR;
+  constexpr int CPR = D / 8;       // 16-byte chunks per K/V row
+  constexpr int KPI = 64 / CPR;    // keys per row-load instruction
+  constexpr int NLD = kKeyTile / KPI;
+  constexpr int ROWH = D;          // halves per staged row (no padding: swizzled)
+  constexpr int TILEH = kKeyTile * ROWH;
+  constexpr int REGION = 2 * TILEH;                // K tile, then V tile
   static_assert(REGION * 2 >= kDecodeRows * D * 4, "wave region must hold its O staging");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * REGION];
-  __shared__ float sm_m[kWaves][kDecodeRows];
-  __shared__ float sm_l[kWaves][kDecodeRows];
-  __shared__ int s_wsum[kWaves];
-  __shared__ int s_found[2];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int lr = lane & 15;        // MFMA row/col index within a 16 block
-  const int lg = lane >> 4;        // 16-lane group
-  const int g = blockIdx.x % p.hkv;
-  const int unit = blockIdx.x / p.hkv;
-  const int S = p.num_splits;
-
-  int b, off;
-  if (p.all_decode) {
-    b = unit / S;
-    off = unit - b * S;
-    if (b >= p.batch) return;
-  } else if (!locate_unit(p, unit, b, off, s_wsum, s_found)) {
-    return;
-  }
-
-  const int cu_b = p.cu_seqlens_q[b];
-  const int q_len = max(0, min(p.cu_seqlens_q[b + 1], p.total_q) - cu_b);
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
   const int group = p.group;
-  const int rows_b = q_len * group;
-  if (rows_b <= 0) return;
-  const bool prefill = !p.all_decode && rows_b > kDecodeRows;
-  const int split = prefill ? 0 : off;
-  const int S_b = prefill ? 1 : S;
-  const int qtile = prefill ? off : 0;
-  const int K_b = max(0, p.cache_seqlens[b]) + (p.appended ? q_len : 0);
+  const int rows_b = si.q_len * group;
+  const int bound = row_key_bound(rows_b - 1, group, si.q_len, si.K_b, p.causal);
 
-  // keys visible to packed row r (bottom-right causal alignment)
-  auto key_bound = [&](int r) -> int {
-    if (!p.causal) return K_b;
-    const int lim = K_b - q_len + r / group + 1;
-    return max(0, min(lim, K_b));
-  };
+  // this split's tiles, then this wave's contiguous share
+  const int n_t = (bound + kKeyTile - 1) / kKeyTile;
+  const int t_begin = (int)((long)split * n_t / S_b);
+  const int t_end = (int)((long)(split + 1) * n_t / S_b);
+  const int key_end = min(t_end * kKeyTile, bound);
+  const int n_w = t_end - t_begin;
+  const int w_begin = t_begin + wave * (n_w >> 2) + min(wave, n_w & 3);
+  const int w_end = w_begin + (n_w >> 2) + (wave < (n_w & 3) ? 1 : 0);
+  // keys of this wave: [w_begin * 32, key_end_w); tiles past w_end (the
+  // pipeline's tail) read nothing and are fully masked
+  const int key_end_w = min(w_end * kKeyTile, key_end);
 
-  const int row0 = prefill ? qtile * kPrefillRows + wave * 16 : 0;
-  const int rows_here = min(kDecodeRows, rows_b - row0);   // may be <= 0 (idle wave)
-  const int wave_bound = rows_here > 0 ? key_bound(row0 + rows_here - 1) : 0;
-
-  // key-tile range: this unit's split of the visible keys, tile aligned
-  const int n_t = (wave_bound + kKeyTile - 1) / kKeyTile;
-  const int chunk = (n_t + S_b - 1) / S_b;
-  const int t_begin = split * chunk;
-  const int t_end = min(t_begin + chunk, n_t);
-  const int key_end = min(t_end * kKeyTile, wave_bound);
-  const int t_first = prefill ? t_begin : t_begin + wave;
-  const int t_step = prefill ? 1 : kWaves;
-
-  // this lane's query row (N index of the MFMAs)
-  const int my_row = row0 + lr;
-  const bool row_ok = lr < rows_here;
-  const int tok = row_ok ? my_row / group : 0;
-  const int h = g * group + (row_ok ? my_row - tok * group : 0);
-  const int row_lim = row_ok ? min(key_bound(my_row), key_end) : 0;
+  const bool row_ok = lr < rows_b;
+  const int tok = row_ok ? lr / group : 0;
+  const int h = g * group + (row_ok ? lr - tok * group : 0);
+  const int row_lim =
+      row_ok ? min(row_key_bound(lr, group, si.q_len, si.K_b, p.causal), key_end_w) : 0;
 
   u32x4 qf[DS];
   {
-    const uint16_t *qrow = p.q + ((long)(cu_b + tok) * p.hq + h) * D;
+    const uint16_t *qrow = p.q + ((long)(si.cu_b + tok) * p.hq + h) * D;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
       qf[ds] = row_ok ? load16(qrow + (ds * 4 + lg) * 8) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  auto load_tile = [&](int t, u32x4 (&kf)[2][DS], u32x4 (&vf)[2][DS]) {
+  const CacheGeom &cg = p.geom;
+  const bool paged = cg.table != nullptr;
+  const int shift = cg.page_shift;
+  const Slab slab = paged ? Slab{(uint32_t)(p.hkv * D * 2) << shift, (long)(p.hkv * D) << shift}
+                          : Slab{(uint32_t)cg.contig_alloc * p.hkv * D * 2,
+                                 (long)cg.contig_alloc * p.hkv * D};
+
+  // load role of this lane: key ld_key of each group of KPI keys, chunk ld_chunk
+  const int ld_key = lane / CPR;
+  const int ld_chunk = lane % CPR;
+  // Page ids of tile t: lane i < NLD reads the table entry of load
+  // instruction i's keys (KPI consecutive keys never straddle a page).  The
+  // read is unconditional; lanes with nothing to read load a harmless word.
+  auto load_ids = [&](int t) -> int {
+    const int key = t * kKeyTile + (lane % NLD) * KPI;
+    const bool ok = paged && lane < NLD && key < key_end_w && (key >> shift) < cg.mpp;
+    const int32_t *src = ok ? cg.table + (long)b * cg.mpp + (key >> shift) : p.cu_seqlens_q;
+    return *src;
+  };
+  // Loop-invariant part of each load's byte offset: the key's row within its
+  // page (a 32-key tile never wraps inside a page of >= 32 keys; with 16-key
+  // pages its upper half starts a new page), kv head g, 16-byte chunk.
+  const uint32_t row_bytes = (uint32_t)p.hkv * D * 2;
+  const int in_page_mask = paged ? min((1 << shift), kKeyTile) - 1 : kKeyTile - 1;
+  const int upper_lane = in_page_mask < kKeyTile - 1 ? (in_page_mask + 1) / KPI : 0;
+  uint32_t lane_off[NLD];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = t * kKeyTile + kb * 16 + lr;
-      const long prow = key < key_end ? physical_row(p.geom, b, key) : -1L;
-      if (prow >= 0) {
-        const long base = (prow * p.hkv + g) * D;
+  for (int i = 0; i < NLD; ++i)
+    lane_off[i] = (uint32_t)((i * KPI + ld_key) & in_page_mask) * row_bytes +
+                  (uint32_t)(g * D + ld_chunk * 8) * 2;
+  auto issue = [&](int t, u32x4 (&kf)[NLD], u32x4 (&vf)[NLD], int ids) {
+    const int key0 = t * kKeyTile;
+    // first row of the tile inside its page (wave-uniform)
+    const uint32_t uni = (uint32_t)(paged ? (key0 & ((1 << shift) - 1)) : key0) * row_bytes;
+    // the tile's one or two pages: those of the first load instruction and of
+    // the first instruction of the tile's upper half (keys 16.., which start a
+    // new page only when pages hold 16 keys)
+    int pg_a = paged ? __builtin_amdgcn_readlane(ids, 0) : b;
+    int pg_b = paged ? __builtin_amdgcn_readlane(ids, upper_lane) : b;
+    const bool ok_a = !paged || (unsigned)pg_a < (unsigned)cg.num_pages;
+    const bool ok_b = !paged || (unsigned)pg_b < (unsigned)cg.num_pages;
+    pg_a = ok_a ? pg_a : 0;
+    pg_b = ok_b ? pg_b : 0;
+    const __amdgpu_buffer_rsrc_t rk_a = page_rsrc(p.k_cache + pg_a * slab.elems, slab.bytes);
+    const __amdgpu_buffer_rsrc_t rv_a = page_rsrc(p.v_cache + pg_a * slab.elems, slab.bytes);
+    const __amdgpu_buffer_rsrc_t rk_b = page_rsrc(p.k_cache + pg_b * slab.elems, slab.bytes);
+    const __amdgpu_buffer_rsrc_t rv_b = page_rsrc(p.v_cache + pg_b * slab.elems, slab.bytes);
+    const int limit = paged ? key_end_w : min(key_end_w, cg.contig_alloc);
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          kf[kb][ds] = load16(p.k_cache + base + (ds * 4 + lg) * 8);
-          vf[kb][ds] = load16(p.v_cache + base + (ds * 4 + lg) * 8);
-        }
-      } else {
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          kf[kb][ds] = u32x4{0u, 0u, 0u, 0u};
-          vf[kb][ds] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
+    for (int i = 0; i < NLD; ++i) {
+      const bool second = paged && (i * KPI) > in_page_mask;   // upper half of a 16-key-page tile
+      const bool ok = (second ? ok_b : ok_a) && key0 + i * KPI + ld_key < limit;
+      const uint32_t off = ok ? lane_off[i] : kOOB;
+      kf[i] = buf_load16_stream(second ? rk_b : rk_a, off, uni);
+      vf[i] = buf_load16_stream(second ? rv_b : rv_a, off, uni);
     }
   };
 
@@ -270,15 +400,30 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   f32x4 o_acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t *ks_ = smem + wave * REGION;   // K tile [32][D], chunk-swizzled rows
+  uint16_t *vs_ = ks_ + TILEH;            // V tile [32][D], chunk-swizzled rows
+  // element offset of (key, 16-byte chunk) in a swizzled tile
+  auto soff = [&](int key, int chunk) { return key * ROWH + ((chunk ^ (key & (CPR - 1))) << 3); };
 
-  uint16_t *vs = smem + wave * REGION;
-  u32x4 kf[2][DS], vf[2][DS];
-  if (t_first < t_end) load_tile(t_first, kf, vf);
+  // per-lane constants of the operand reads
+  const uint16_t *k_rd[2][DS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) k_rd[kb][ds] = ks_ + soff(kb * 16 + lr, ds * 4 + lg);
 
-  for (int t = t_first; t < t_end; t += t_step) {
-    u32x4 kn[2][DS], vn[2][DS];
-    const int tn = t + t_step;
-    if (tn < t_end) load_tile(tn, kn, vn);
+  auto step = [&](int t, u32x4 (&kf)[NLD], u32x4 (&vf)[NLD], int &ids) {
+    // stage the tile's rows into LDS
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int o = soff(i * KPI + ld_key, ld_chunk);
+      store16(ks_ + o, kf[i]);
+      store16(vs_ + o, vf[i]);
+    }
+    // registers of tile t are free: start tile t + 2 (its page ids arrived two
+    // steps ago) and fetch the page ids of tile t + 4
+    issue(t + 2, kf, vf, ids);
+    ids = load_ids(t + 4);
 
     // S^T block per 16 keys: lane holds keys kb*16 + 4*lg + i of row lr
     f32x4 sc[2];
@@ -286,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
     for (int kb = 0; kb < 2; ++kb) {
       sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) sc[kb] = Elt<DT>::mfma16(kf[kb][ds], qf[ds], sc[kb]);
+      for (int ds = 0; ds < DS; ++ds) sc[kb] = Elt<DT>::mfma16(load16(k_rd[kb][ds]), qf[ds], sc[kb]);
     }
 
     float s[8];
@@ -304,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
     tmax = group4_max(tmax);
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_use);
     float ps[8];
     float psum = 0.f;
 #pragma unroll
@@ -314,18 +459,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
     }
     l_part = l_part * alpha + psum;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {   // rescale only when some row's maximum moved
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o_acc[db] *= alpha;
-
-    // V tile -> this wave's LDS region, row-major [key][dim]
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        store16(vs + (kb * 16 + lr) * VSTR + (ds * 4 + lg) * 8, vf[kb][ds]);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int db = 0; db < DB; ++db) o_acc[db] *= alpha;
+    }
 
     // P^T operand: element e <-> key (e / 4) * 16 + 4 * lg + e % 4
     u32x4 pb, pb_lo;
@@ -341,38 +478,42 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
         pb_lo[e] = pack2<DT>(ps[2 * e] - h0, ps[2 * e + 1] - h1);
       }
     }
-
+    // V^T operand: keys 4*lg .. +3 and 16 + 4*lg .. +3 of dim db*16 + lr; lane
+    // lr addresses row k0 + lr/4, dims db*16 + 4*(lr%4) .. +3 (8 bytes)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      u32x4 va;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int k0 = ((2 * e) >> 2) * 16 + 4 * lg + ((2 * e) & 3);
-        const int k1 = ((2 * e + 1) >> 2) * 16 + 4 * lg + ((2 * e + 1) & 3);
-        const uint32_t v0 = vs[k0 * VSTR + db * 16 + lr];
-        const uint32_t v1 = vs[k1 * VSTR + db * 16 + lr];
-        va[e] = v0 | (v1 << 16);
-      }
+      const int r0 = 4 * lg + (lr >> 2);
+      const int r1 = r0 + 16;
+      const int ch = 2 * db + ((lr & 3) >> 1);
+      const int half = (lr & 1) * 4;
+      const u32x2 a0 = lds_read_tr16(vs_ + soff(r0, ch) + half);
+      const u32x2 a1 = lds_read_tr16(vs_ + soff(r1, ch) + half);
+      const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]};
       o_acc[db] = Elt<DT>::mfma16(va, pb, o_acc[db]);
       if constexpr (DT == kBF16) o_acc[db] = Elt<DT>::mfma16(va, pb_lo, o_acc[db]);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        kf[kb][ds] = kn[kb][ds];
-        vf[kb][ds] = vn[kb][ds];
-      }
+  // Every load below is issued unconditionally (masked lanes read nothing),
+  // so two tiles stay in flight per wave with exact waits.
+  if (w_begin < w_end) {
+    u32x4 ka[NLD], va_[NLD], kb_[NLD], vb_[NLD];
+    int ids_a = load_ids(w_begin);
+    int ids_b = load_ids(w_begin + 1);
+    issue(w_begin, ka, va_, ids_a);
+    ids_a = load_ids(w_begin + 2);
+    issue(w_begin + 1, kb_, vb_, ids_b);
+    ids_b = load_ids(w_begin + 3);
+    for (int t = w_begin; t < w_end; t += 2) {
+      step(t, ka, va_, ids_a);
+      step(t + 1, kb_, vb_, ids_b);   // past w_end: an empty, fully masked tile
+    }
   }
 
   const float l_row = group4_sum(l_part);
 
-  // ---- epilogue: stage each wave's (m, l, O) in LDS, then write rows ----
-  float *stage = reinterpret_cast<float *>(vs);   // [16 rows][D] fp32, own region
+  // ---- epilogue: stage each wave's (m, l, O) in LDS, merge, write ----
+  float *stage = reinterpret_cast<float *>(ks_);   // [16 rows][D] fp32, own region
 #pragma unroll
   for (int db = 0; db < DB; ++db)
     *reinterpret_cast<f32x4 *>(stage + lr * D + db * 16 + lg * 4) = o_acc[db];
@@ -385,74 +526,325 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdParams p) {
   constexpr int CH = D / 16;       // dims per thread in the write-out
   const int orow = tid >> 4;       // 0..15
   const int oc = tid & 15;
-  const int nblk = prefill ? kWaves : 1;
-  for (int rb = 0; rb < nblk; ++rb) {
-    const int prow = (prefill ? qtile * kPrefillRows + rb * 16 : 0) + orow;
-    if (prow >= rows_b) continue;
-    const int w_lo = prefill ? rb : 0;
-    const int w_hi = prefill ? rb + 1 : kWaves;
-    float M = kNegInf;
-    for (int w = w_lo; w < w_hi; ++w) M = fmaxf(M, sm_m[w][orow]);
-    float acc[CH];
+  if (orow >= rows_b) return;
+  float M = kNegInf;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) acc[c] = 0.f;
-    float L = 0.f;
-    if (M != kNegInf) {
-      for (int w = w_lo; w < w_hi; ++w) {
-        const float mw = sm_m[w][orow];
-        const float wt = fast_exp2(mw - M);   // 0 for waves that saw nothing
-        L += wt * sm_l[w][orow];
-        const float *src = reinterpret_cast<const float *>(smem + w * REGION) + orow * D + oc * CH;
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][orow]);
+  float acc[CH];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) acc[c] += wt * src[c];
-      }
+  for (int c = 0; c < CH; ++c) acc[c] = 0.f;
+  float L = 0.f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = fast_exp2(sm_m[w][orow] - M);   // 0 for waves that saw nothing
+      L += wt * sm_l[w][orow];
+      const float *src = reinterpret_cast<const float *>(smem + w * REGION) + orow * D + oc * CH;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) acc[c] += wt * src[c];
     }
-    const bool empty = !(L > 0.f);
-    const float inv = empty ? 0.f : 1.f / L;
-    const float lse_val = empty ? kNegInf : (M + __builtin_log2f(L)) * kLn2;
-    const int tk = prow / group;
-    const int hp = g * group + (prow - tk * group);
-    const long ridx = (long)(cu_b + tk) * p.hq + hp;
-    if (S_b == 1) {
-      uint16_t *dst = p.out + ridx * D + oc * CH;
-      if constexpr (CH == 8) {
-        u32x4 pk;
+  }
+  const bool empty = !(L > 0.f);
+  const float inv = empty ? 0.f : 1.f / L;
+  const float lse_val = empty ? kNegInf : (M + __builtin_log2f(L)) * kLn2;
+  const int tk = orow / group;
+  const int hp = g * group + (orow - tk * group);
+  const long ridx = (long)(si.cu_b + tk) * p.hq + hp;
+  if (S_b == 1) {
+    uint16_t *dst = p.out + ridx * D + oc * CH;
+    if constexpr (CH == 8) {
+      u32x4 pk;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = pack2<DT>(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-        store16(dst, pk);
-      } else {
-        u32x2 pk;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) pk[e] = pack2<DT>(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-        *reinterpret_cast<u32x2 *>(dst) = pk;
-      }
-      if (oc == 0) p.lse[ridx] = lse_val;
+      for (int e = 0; e < 4; ++e) pk[e] = pack2<DT>(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+      store16(dst, pk);
     } else {
-      const long pidx = (long)split * p.total_q * p.hq + ridx;
-      float *dst = p.o_part + pidx * D + oc * CH;
+      u32x2 pk;
 #pragma unroll
-      for (int c = 0; c < CH; c += 4)
-        *reinterpret_cast<f32x4 *>(dst + c) =
-            f32x4{acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
-      if (oc == 0) p.lse_part[pidx] = lse_val;
+      for (int e = 0; e < 2; ++e) pk[e] = pack2<DT>(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+      *reinterpret_cast<u32x2 *>(dst) = pk;
     }
+    if (oc == 0) p.lse[ridx] = lse_val;
+  } else {
+    const long pidx = (long)split * p.total_q * p.hq + ridx;
+    float *dst = p.o_part + pidx * D + oc * CH;
+#pragma unroll
+    for (int c = 0; c < CH; c += 4)
+      *reinterpret_cast<f32x4 *>(dst + c) =
+          f32x4{acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
+    if (oc == 0) p.lse_part[pidx] = lse_val;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV combine: per (token, q head) row, lse = log(sum_s exp(lse_s)) and
+// Prefill unit: 128 packed rows (32 per wave) of one sequence and kv head,
+// every key those rows can see, one split.  64-key tiles of K and V are
+// gathered page by page by the whole workgroup into double-buffered LDS (the
+// next tile's global loads are in flight while the current tile is
+// computed; one barrier per tile):
+//   S^T = K Q^T    32x32x16 MFMA, keys on M, Q held in registers;
+//   softmax        online, per row, in log2 units; the accumulator is only
+//                  rescaled when some row's maximum moved;
+//   O^T += V^T P^T 32x32x16 MFMA, V^T read through transposing LDS reads.
+// Tiles wholly below every row's causal limit skip the mask.
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, const int g,
+                                             const int qtile, const SeqInfo si, uint16_t *smem) {
+  constexpr int QS = D / 16;        // k-steps over D (16 dims each)
+  constexpr int DBP = D / 32;       // 32-dim blocks of O^T
+  constexpr int KSTR = D + 8;       // LDS row stride (halves)
+  constexpr int TILE_H = kPTile * KSTR;
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int NCH = kPTile * CPR / kThreads;
+  static_assert(NCH * kThreads == kPTile * CPR, "tile chunks must divide the workgroup");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n32 = lane & 31;       // MFMA column (row of this wave)
+  const int hh = lane >> 5;        // k half
+  const int group = p.group;
+  const int rows_b = si.q_len * group;
+  const int wg_row0 = qtile * kPrefillRows;
+  const int wg_rows = min(kPrefillRows, rows_b - wg_row0);
+  const int wg_bound = row_key_bound(wg_row0 + wg_rows - 1, group, si.q_len, si.K_b, p.causal);
+  const int n_t = (wg_bound + kPTile - 1) / kPTile;
+
+  const int row0 = wg_row0 + wave * 32;
+  const int rows_here = min(32, rows_b - row0);   // <= 0: idle wave (loads and barriers only)
+  const int wave_bound =
+      rows_here > 0 ? row_key_bound(row0 + rows_here - 1, group, si.q_len, si.K_b, p.causal) : 0;
+  const int first_bound =
+      rows_here > 0 ? row_key_bound(row0, group, si.q_len, si.K_b, p.causal) : 0;
+  const int my_row = row0 + n32;
+  const bool row_ok = n32 < rows_here;
+  const int tok = row_ok ? my_row / group : 0;
+  const int h = g * group + (row_ok ? my_row - tok * group : 0);
+  const int row_lim = row_ok ? row_key_bound(my_row, group, si.q_len, si.K_b, p.causal) : 0;
+
+  u32x4 qf[QS];
+  {
+    const uint16_t *qrow = p.q + ((long)(si.cu_b + tok) * p.hq + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < QS; ++ds)
+      qf[ds] = row_ok ? load16(qrow + ds * 16 + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const CacheGeom &cg = p.geom;
+  const bool paged = cg.table != nullptr;
+  const int shift = cg.page_shift;
+  const Slab slab = paged ? Slab{(uint32_t)(p.hkv * D * 2) << shift, (long)(p.hkv * D) << shift}
+                          : Slab{(uint32_t)cg.contig_alloc * p.hkv * D * 2,
+                                 (long)cg.contig_alloc * p.hkv * D};
+  // Tile loads: instruction r of wave w fetches whole rows of keys
+  // t*64 + (w*64 + r*256)/CPR + lane/CPR (64*16/(2D) keys, one page).
+  // Page ids of tile t: lane r < NCH reads the entry of instruction r.
+  auto load_ids = [&](int t) -> int {
+    const int key = t * kPTile + (wave * 64 + (lane % NCH) * kThreads) / CPR;
+    const bool ok = paged && lane < NCH && key < wg_bound && (key >> shift) < cg.mpp;
+    const int32_t *src = ok ? cg.table + (long)b * cg.mpp + (key >> shift) : p.cu_seqlens_q;
+    return *src;
+  };
+  u32x4 kst[NCH], vst[NCH];
+  auto gload = [&](int t, int ids) {
+#pragma unroll
+    for (int r = 0; r < NCH; ++r) {
+      const int c = tid + r * kThreads;
+      const int key = t * kPTile + c / CPR;
+      const int col = c % CPR;
+      int page = paged ? __builtin_amdgcn_readlane(ids, r) : b;
+      const bool page_ok = !paged || (unsigned)page < (unsigned)cg.num_pages;
+      page = page_ok ? page : 0;
+      const int slot = paged ? (key & ((1 << shift) - 1)) : key;
+      const bool ok = page_ok && key < wg_bound && (paged || key < cg.contig_alloc);
+      const uint32_t off = ok ? (uint32_t)(((slot * p.hkv + g) * D + col * 8) * 2) : kOOB;
+      kst[r] = buf_load16(page_rsrc(p.k_cache + page * slab.elems, slab.bytes), off);
+      vst[r] = buf_load16(page_rsrc(p.v_cache + page * slab.elems, slab.bytes), off);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t *kb = smem + buf * 2 * TILE_H;
+    uint16_t *vb = kb + TILE_H;
+#pragma unroll
+    for (int r = 0; r < NCH; ++r) {
+      const int c = tid + r * kThreads;
+      const int off = (c / CPR) * KSTR + (c % CPR) * 8;
+      store16(kb + off, kst[r]);
+      store16(vb + off, vst[r]);
+    }
+  };
+
+  f32x16 o_acc[DBP];
+#pragma unroll
+  for (int db = 0; db < DBP; ++db) o_acc[db] = f32x16{};
+  float m_run = kNegInf;
+  float l_part = 0.f;
+
+  // Loads are unconditional (tiles past the end read nothing); the only wait
+  // for global data is before staging the next tile, after this one's math.
+  int ids_next = 0;
+  if (n_t > 0) {
+    const int ids0 = load_ids(0);
+    gload(0, ids0);
+    ids_next = load_ids(1);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_t; ++t) {
+    const int buf = t & 1;
+    const int ids_after = load_ids(t + 2);
+    gload(t + 1, ids_next);
+    if (t * kPTile < wave_bound) {
+      const uint16_t *kt = smem + buf * 2 * TILE_H;
+      const uint16_t *vt = kt + TILE_H;
+      f32x16 sc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sc[kb] = f32x16{};
+        const uint16_t *krow = kt + (kb * 32 + n32) * KSTR + 8 * hh;
+#pragma unroll
+        for (int ds = 0; ds < QS; ++ds)
+          sc[kb] = Elt<DT>::mfma32(load16(krow + ds * 16), qf[ds], sc[kb]);
+      }
+      // scale, mask, running max.  Lane (n32, hh) element i of block kb is key
+      // t*64 + kb*32 + (i/4)*8 + 4*hh + i%4 of row n32.
+      const bool full = (t + 1) * kPTile <= first_bound;
+      float tmax = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float v = sc[kb][i] * p.scale_log2;
+          if (!full) {
+            const int key = t * kPTile + kb * 32 + (i >> 2) * 8 + 4 * hh + (i & 3);
+            v = key < row_lim ? v : kNegInf;
+          }
+          sc[kb][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_use);
+      float psum = 0.f;
+      u32x4 pb[4], pb_lo[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(sc[ks >> 1][(ks & 1) * 8 + 2 * e] - m_use);
+          const float p1 = fast_exp2(sc[ks >> 1][(ks & 1) * 8 + 2 * e + 1] - m_use);
+          psum += p0 + p1;
+          pb[ks][e] = pack2<DT>(p0, p1);
+          if constexpr (DT == kBF16) {
+            pb_lo[ks][e] = pack2<DT>(p0 - Elt<DT>::to_f32((uint16_t)(pb[ks][e] & 0xffffu)),
+                                     p1 - Elt<DT>::to_f32((uint16_t)(pb[ks][e] >> 16)));
+          }
+        }
+      }
+      l_part = l_part * alpha + psum;
+      m_run = m_new;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < DBP; ++db) o_acc[db] *= alpha;
+      }
+      // PV: lane group G reads dims db*32 + 16*(G&1) + 0..15, keys of k half G>>1
+      const int G = lane >> 4;
+      const int s16 = lane & 15;
+      const uint16_t *vtr = vt + (4 * (G >> 1) + (s16 >> 2)) * KSTR + 16 * (G & 1) + 4 * (s16 & 3);
+#pragma unroll
+      for (int db = 0; db < DBP; ++db) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x2 a0 = lds_read_tr16(vtr + (ks * 16) * KSTR + db * 32);
+          const u32x2 a1 = lds_read_tr16(vtr + (ks * 16 + 8) * KSTR + db * 32);
+          const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]};
+          o_acc[db] = Elt<DT>::mfma32(va, pb[ks], o_acc[db]);
+          if constexpr (DT == kBF16) o_acc[db] = Elt<DT>::mfma32(va, pb_lo[ks], o_acc[db]);
+        }
+      }
+    }
+    lstore(buf ^ 1);
+    __syncthreads();
+    ids_next = ids_after;
+  }
+
+  if (!row_ok) return;
+  const float L = l_part + __shfl_xor(l_part, 32, 64);
+  const bool empty = !(L > 0.f);
+  const float inv = empty ? 0.f : 1.f / L;
+  const long ridx = (long)(si.cu_b + tok) * p.hq + h;
+  uint16_t *dst = p.out + ridx * D;
+#pragma unroll
+  for (int db = 0; db < DBP; ++db) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      u32x2 pk;
+      pk[0] = pack2<DT>(o_acc[db][q4 * 4 + 0] * inv, o_acc[db][q4 * 4 + 1] * inv);
+      pk[1] = pack2<DT>(o_acc[db][q4 * 4 + 2] * inv, o_acc[db][q4 * 4 + 3] * inv);
+      *reinterpret_cast<u32x2 *>(dst + db * 32 + q4 * 8 + 4 * hh) = pk;
+    }
+  }
+  if (hh == 0) p.lse[ridx] = empty ? kNegInf : (m_run + __builtin_log2f(L)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Unified attention kernel: one workgroup = one work unit.  Decode units and
+// prefill units of any mix of sequences share the grid; each workgroup finds
+// its unit from the device metadata (see locate_unit) and runs the matching
+// path.  Key tiles (32 keys in decode, 64 in prefill) and split boundaries
+// depend only on lengths, never on the page size or on which physical pages
+// hold the keys, so results are bit-identical across page sizes and page
+// relabellings.
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kPTile * (D + 8)];
+  __shared__ float sm_m[kWaves][kDecodeRows];
+  __shared__ float sm_l[kWaves][kDecodeRows];
+  __shared__ int s_wsum[kWaves];
+  __shared__ int s_found[3];
+
+  const int g = blockIdx.x % p.hkv;
+  const int unit = blockIdx.x / p.hkv;
+  UnitInfo u;
+  if (p.all_decode && p.num_splits == 1) {
+    u.b = unit;
+    u.off = 0;
+    u.splits = 1;
+    if (u.b >= p.batch) return;
+  } else if (!locate_unit(p, unit, u, s_wsum, s_found)) {
+    return;
+  }
+  const SeqInfo si = seq_info(p, u.b);
+  const int rows_b = si.q_len * p.group;
+  if (rows_b <= 0) return;
+  if (p.all_decode || rows_b <= kDecodeRows) {
+    if (g == 0 && u.off == 0 && p.split_count != nullptr && threadIdx.x == 0)
+      p.split_count[u.b] = u.splits;
+    decode_unit<DT, D>(p, u.b, g, u.off, u.splits, si, smem, sm_m, sm_l);
+  } else {
+    const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
+    prefill_unit<DT, D>(p, u.b, g, n_qt - 1 - u.off, si, smem);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV combine: per (token, q head) row of a decode-mode sequence with
+// more than one split, lse = log(sum_s exp(lse_s)) and
 // out = sum_s exp(lse_s - lse) * o_s over the splits that saw a key; a row
-// whose splits were all empty gets out = 0, lse = -inf.  Only rows of decode
-// units carry partials; rows of prefill units were written directly and are
-// skipped.  One wave per row.
+// whose splits were all empty gets out = 0, lse = -inf.  Rows of prefill
+// units and of single-split sequences were written directly and are skipped.
+// One wave per row.
 // ---------------------------------------------------------------------------
 struct CombineParams {
   const float *o_part;
   const float *lse_part;
+  const int32_t *split_count;
   const int32_t *cu_seqlens_q;
   uint16_t *out;
   float *lse;
-  int batch, total_q, hq, group, num_splits, all_decode;
+  int batch, total_q, hq, group, all_decode;
 };
 
 template <int DT, int D>
@@ -461,20 +853,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   const long row = (long)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= (long)p.total_q * p.hq) return;
   const int token = (int)(row / p.hq);
-  if (!p.all_decode) {
-    int lo = 0, hi = p.batch;   // largest b with cu[b] <= token
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.cu_seqlens_q[mid] <= token) lo = mid; else hi = mid;
-    }
-    const int q_len = p.cu_seqlens_q[lo + 1] - p.cu_seqlens_q[lo];
-    if (token >= p.cu_seqlens_q[lo + 1]) return;   // past cu[batch]
-    if (q_len * p.group > kDecodeRows) return;     // prefill row: already final
-  } else if (token >= p.cu_seqlens_q[p.batch]) {
-    return;
+  int lo = 0, hi = p.batch;   // largest b with cu[b] <= token
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.cu_seqlens_q[mid] <= token) lo = mid; else hi = mid;
   }
+  const int end = min(p.cu_seqlens_q[lo + 1], p.total_q);
+  if (token >= end) return;
+  const int q_len = end - p.cu_seqlens_q[lo];
+  if (!p.all_decode && q_len * p.group > kDecodeRows) return;   // prefill row: already final
+  const int S = p.split_count[lo];
+  if (S <= 1) return;                                            // written directly
   const long stride = (long)p.total_q * p.hq;
-  const int S = p.num_splits;
   float M = kNegInf;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, p.lse_part[s * stride + row]);
 #pragma unroll

@@ -16,14 +16,15 @@ namespace {
 
 using pa::kThreads;
 
-constexpr int kMaxSplits = 128;
+constexpr int kMaxSplits = pa::kMaxSplits;
 
 struct Plan {
-  int splits = 1;
+  int splits = 1;         // split budget: average splits per decode sequence
+  int max_splits = 1;     // most splits one sequence can receive
   bool all_decode = true;
   long grid = 0;          // attention workgroups
   size_t ws_bytes = 0;
-  size_t o_part_off = 0, lse_part_off = 0;
+  size_t o_part_off = 0, lse_part_off = 0, count_off = 0;
   int max_seqlen_k = 0;
 };
 
@@ -33,8 +34,9 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline long cdiv(long a, long b) { return (a + b - 1) / b; }
 
 // Argument checks shared by every entry point.  `append_only` relaxes the
-// fields the append step does not read.
-pa_status validate(const pa_fwd_args *a, bool append_only) {
+// fields the append step does not read; `sizes_only` skips the data pointers
+// (used by the host-only sizing queries).
+pa_status validate(const pa_fwd_args *a, bool append_only, bool sizes_only = false) {
   if (a == nullptr) return PA_ERR_NULL;
   if (a->dtype != PA_F16 && a->dtype != PA_BF16) return PA_ERR_DTYPE;
   if (a->reserved0 != 0) return PA_ERR_SHAPE;
@@ -43,15 +45,20 @@ pa_status validate(const pa_fwd_args *a, bool append_only) {
   if (a->total_q > 0 && a->max_seqlen_q < 1) return PA_ERR_SHAPE;
   if (a->num_heads_kv < 1) return PA_ERR_SHAPE;
   if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  // kernels address one page (or one contiguous sequence) with 32-bit byte
+  // offsets: it must span less than 2 GiB
+  const long row_bytes = (long)a->num_heads_kv * a->head_dim * 2;
   if (a->block_table != nullptr) {
     if (!is_pow2(a->page_size) || a->page_size < 16 || a->page_size > 256)
       return PA_ERR_UNSUPPORTED;
     if (a->num_pages < 1 || a->max_pages_per_seq < 1) return PA_ERR_SHAPE;
-  } else if (a->contig_alloc < 1) {
-    return PA_ERR_SHAPE;
+    if (row_bytes * a->page_size >= (1L << 31)) return PA_ERR_UNSUPPORTED;
+  } else {
+    if (a->contig_alloc < 1) return PA_ERR_SHAPE;
+    if (row_bytes * a->contig_alloc >= (1L << 31)) return PA_ERR_UNSUPPORTED;
   }
-  if (a->k_cache == nullptr || a->v_cache == nullptr || a->cache_seqlens == nullptr ||
-      a->cu_seqlens_q == nullptr)
+  if (!sizes_only && (a->k_cache == nullptr || a->v_cache == nullptr ||
+                     a->cache_seqlens == nullptr || a->cu_seqlens_q == nullptr))
     return PA_ERR_NULL;
   if ((a->k_new == nullptr) != (a->v_new == nullptr)) return PA_ERR_NULL;
   if (append_only) {
@@ -62,7 +69,8 @@ pa_status validate(const pa_fwd_args *a, bool append_only) {
   if (a->causal != 0 && a->causal != 1) return PA_ERR_SHAPE;
   if (a->num_splits < 0 || a->num_splits > kMaxSplits) return PA_ERR_SHAPE;
   if (!(a->softmax_scale == a->softmax_scale)) return PA_ERR_SHAPE;   // NaN
-  if (a->q == nullptr || a->out == nullptr || a->softmax_lse == nullptr) return PA_ERR_NULL;
+  if (!sizes_only && (a->q == nullptr || a->out == nullptr || a->softmax_lse == nullptr))
+    return PA_ERR_NULL;
   return PA_OK;
 }
 
@@ -104,10 +112,16 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
   if (!pl.all_decode) units_per_head += cdiv((long)a->total_q * group, pa::kPrefillRows);
   pl.grid = units_per_head * a->num_heads_kv;
   if (pl.splits > 1) {
+    // the device shares the budget by sequence length (one split each, the
+    // rest in proportion to key tiles): one sequence can get up to
+    // 1 + batch * (splits - 1), capped at kMaxSplits
+    const long most = 1 + (long)a->batch * (pl.splits - 1);
+    pl.max_splits = (int)std::min<long>(most, kMaxSplits);
     const size_t rows = (size_t)a->total_q * a->num_heads_q;
     pl.o_part_off = 0;
-    pl.lse_part_off = align_up((size_t)pl.splits * rows * a->head_dim * sizeof(float), 256);
-    pl.ws_bytes = align_up(pl.lse_part_off + (size_t)pl.splits * rows * sizeof(float), 256);
+    pl.lse_part_off = align_up((size_t)pl.max_splits * rows * a->head_dim * sizeof(float), 256);
+    pl.count_off = align_up(pl.lse_part_off + (size_t)pl.max_splits * rows * sizeof(float), 256);
+    pl.ws_bytes = align_up(pl.count_off + (size_t)a->batch * sizeof(int32_t), 256);
   }
   return pl;
 }
@@ -159,6 +173,7 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   char *ws = static_cast<char *>(a->workspace);
   p.o_part = pl.splits > 1 ? reinterpret_cast<float *>(ws + pl.o_part_off) : nullptr;
   p.lse_part = pl.splits > 1 ? reinterpret_cast<float *>(ws + pl.lse_part_off) : nullptr;
+  p.split_count = pl.splits > 1 ? reinterpret_cast<int32_t *>(ws + pl.count_off) : nullptr;
   p.batch = a->batch;
   p.total_q = a->total_q;
   p.hq = a->num_heads_q;
@@ -179,6 +194,7 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
     pa::CombineParams c;
     c.o_part = p.o_part;
     c.lse_part = p.lse_part;
+    c.split_count = p.split_count;
     c.cu_seqlens_q = a->cu_seqlens_q;
     c.out = p.out;
     c.lse = p.lse;
@@ -186,7 +202,6 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
     c.total_q = a->total_q;
     c.hq = a->num_heads_q;
     c.group = group;
-    c.num_splits = pl.splits;
     c.all_decode = pl.all_decode;
     const long rows = (long)a->total_q * a->num_heads_q;
     const long blocks = cdiv(rows, pa::kWaves);
@@ -230,12 +245,12 @@ int32_t paged_attn_num_splits(int32_t batch, int32_t total_q, int32_t num_heads_
 }
 
 int32_t paged_attn_splits_for(const pa_fwd_args *args) {
-  if (validate(args, false) != PA_OK) return -1;
+  if (validate(args, false, true) != PA_OK) return -1;
   return make_plan(args, device_cus()).splits;
 }
 
 size_t paged_attn_workspace_size(const pa_fwd_args *args) {
-  if (validate(args, false) != PA_OK) return 0;
+  if (validate(args, false, true) != PA_OK) return 0;
   return make_plan(args, device_cus()).ws_bytes;
 }
 

@@ -133,3 +133,25 @@ def test_split_heuristic_properties():
     # degenerate inputs
     assert ns(0, 0, 1, 1, 64, 1, 10, 256) == 1
     assert ns(4, 4, 4, 4, 64, 1, 0, 256) == 1
+
+
+def test_sizing_queries_ignore_data_pointers():
+    a = valid_args(num_splits=3)
+    for f in ("q", "k_cache", "v_cache", "block_table", "cache_seqlens", "cu_seqlens_q", "out",
+              "softmax_lse"):
+        setattr(a, f, None)
+    a.contig_alloc = 256          # no table -> contiguous mode sizes
+    assert pa.paged_attn_splits_for(a) == 3
+    assert pa.paged_attn_workspace_size(a) > 0
+    assert call_fwd(a) == 1       # the forward call itself still needs its pointers
+
+
+def test_slabs_of_two_gib_or_more_are_rejected():
+    # one page of 256 tokens x 64 kv heads x 128 dims x 2 B = 4 MiB is fine (the
+    # call then stops at the missing workspace, before any launch)
+    assert call_fwd(valid_args(page_size=256, num_heads_q=64, num_heads_kv=64,
+                               head_dim=128, num_splits=4)) == 5
+    # a contiguous allocation of 2^31 bytes per sequence is not
+    a = valid_args(block_table=None, contig_alloc=1 << 20, num_heads_q=8, num_heads_kv=8,
+                   head_dim=128)
+    assert call_fwd(a) == 4
