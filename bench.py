@@ -66,6 +66,33 @@ def causal_flops(case):
     return 4 * case.head_dim * case.num_heads_q * total
 
 
+KERNEL_SOURCES = ("paged_kv_cache_lds_amd/csrc/pa_device.h", "paged_kv_cache_lds_amd/csrc/pa_kernels.h",
+                  "paged_kv_cache_lds_amd/csrc/paged_attn.hip")
+TRAFFIC_PROFILE = "profiles/attn_fwd_mha_decode_b256_ctx4096.txt"
+
+
+def measured_traffic(batch, ctx):
+    """HBM bytes per attention launch measured with rocprofv3 PMC counters
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated) on the default workload, taken
+    from the committed profile summary -- or None if the workload differs or
+    the kernel sources changed since the counters were taken."""
+    import hashlib
+    if (batch, ctx) != (256, 4096):
+        return None
+    try:
+        text = open(os.path.join(ROOT, TRAFFIC_PROFILE)).read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines()
+                  if line.startswith(("kernel_source_sha256:", "traffic_bytes_per_launch:")))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if fields.get("kernel_source_sha256", "").strip() != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"].strip())
+
+
 def time_calls(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
@@ -309,7 +336,8 @@ def main():
     attn_bytes = algorithmic_bytes(attn_case)
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(args.batch, args.ctx),
                 "kernel": "attn_fwd_kernel<f16,128>", "launch_ms": round(attn_ms, 4),
                 "bytes_per_launch": attn_bytes, "splits": splits}
 
