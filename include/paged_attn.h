@@ -90,8 +90,9 @@ typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
  *   mode: K_b <= contig_alloc); the page ids read lie in [0, num_pages);
  *   append targets of different sequences are distinct slots; k_new/v_new do
  *   not alias the caches.  Device code never reads outside the table row or
- *   the pool: a key whose page id is out of range is treated as absent and an
- *   append to such a slot is dropped.
+ *   the pool: a key whose page id is out of range is read as a zero K row and
+ *   a zero V row (no error is raised; the result is then unspecified beyond
+ *   being finite), and an append to such a slot is dropped.
  */
 typedef struct pa_fwd_args {
   int32_t dtype;             /* pa_dtype */

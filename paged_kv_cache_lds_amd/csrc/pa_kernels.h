@@ -17,8 +17,9 @@ constexpr int kThreads = 256;     // four wave64 per workgroup
 constexpr int kWaves = 4;
 constexpr int kKeyTile = 32;      // decode: keys per wave main-loop iteration
 constexpr int kDecodeRows = 16;   // packed (token, q-head) rows of a decode unit
-constexpr int kPrefillRows = 128; // rows of a prefill unit: 32 per wave
-constexpr int kPTile = 64;        // prefill: keys per workgroup main-loop iteration
+constexpr int kPrefillRB = 1;     // 32-row MFMA blocks per wave in a prefill unit
+constexpr int kPrefillRows = 32 * kPrefillRB * kWaves;   // rows of a prefill unit
+constexpr int kPTile = 32;        // prefill: keys per workgroup main-loop iteration
 constexpr int kMaxSplits = 128;
 constexpr int kWindow = 64;       // block-table entries a wave holds at once (one per lane)
 
@@ -577,56 +578,73 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
 
 // ---------------------------------------------------------------------------
 // Prefill unit: 128 packed rows (32 per wave) of one sequence and kv head,
-// every key those rows can see, one split.  64-key tiles of K and V are
-// gathered page by page by the whole workgroup into double-buffered LDS (the
-// next tile's global loads are in flight while the current tile is
-// computed; one barrier per tile):
-//   S^T = K Q^T    32x32x16 MFMA, keys on M, Q held in registers;
-//   softmax        online, per row, in log2 units; the accumulator is only
-//                  rescaled when some row's maximum moved;
-//   O^T += V^T P^T 32x32x16 MFMA, V^T read through transposing LDS reads.
-// Tiles wholly below every row's causal limit skip the mask.
+// every key those rows can see, one split.  32-key K and V tiles are
+// gathered page by page by the whole workgroup (unconditional buffer loads,
+// page ids fetched a tile ahead) into LDS rings - two K slots, three V slots,
+// one barrier per tile - and each iteration overlaps two tiles in every wave:
+//   S^T(t+1) = K Q^T   32x32x16 MFMA (keys on M)
+//   softmax(t)         online, log2 units, one fma + exp2 per score
+//   O^T += V^T P^T(t)  32x32x16 MFMA, V^T from transposing LDS reads
+// Tiles every row of the workgroup sees in full run in a branch-free main
+// loop (mask-free, so the next tile's MFMAs and this tile's VALU share one
+// basic block); the tiles on the causal diagonal follow in a masked tail.
+// The running maximum is only moved when it grows by more than 2^8 (the
+// stale maximum stays an exact common reference for the sum and the
+// accumulator, and probabilities stay <= 256), so rescaling is rare.  LDS
+// rows are padded (K: D+8, V: D+32 halves) so every operand read is a lane
+// base plus an immediate offset and conflict-free.
 // ---------------------------------------------------------------------------
+constexpr float kRescaleThreshold = 8.f;   // log2 units
+
 template <int DT, int D>
 __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, const int g,
                                              const int qtile, const SeqInfo si, uint16_t *smem) {
   constexpr int QS = D / 16;        // k-steps over D (16 dims each)
   constexpr int DBP = D / 32;       // 32-dim blocks of O^T
-  constexpr int KSTR = D + 8;       // LDS row stride (halves)
-  constexpr int TILE_H = kPTile * KSTR;
+  constexpr int RB = kPrefillRB;    // 32-row blocks per wave
   constexpr int CPR = D / 8;        // 16-byte chunks per row
   constexpr int NCH = kPTile * CPR / kThreads;
+  constexpr int KSTR = D + 8;       // padded LDS row strides (halves)
+  constexpr int VSTR = D + 32;
+  constexpr int KSLOT = kPTile * KSTR;
+  constexpr int VSLOT = kPTile * VSTR;
   static_assert(NCH * kThreads == kPTile * CPR, "tile chunks must divide the workgroup");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n32 = lane & 31;       // MFMA column (row of this wave)
+  const int n32 = lane & 31;       // MFMA column (row within a 32-row block)
   const int hh = lane >> 5;        // k half
   const int group = p.group;
   const int rows_b = si.q_len * group;
   const int wg_row0 = qtile * kPrefillRows;
   const int wg_rows = min(kPrefillRows, rows_b - wg_row0);
   const int wg_bound = row_key_bound(wg_row0 + wg_rows - 1, group, si.q_len, si.K_b, p.causal);
+  const int wg_first = row_key_bound(wg_row0, group, si.q_len, si.K_b, p.causal);
   const int n_t = (wg_bound + kPTile - 1) / kPTile;
+  const int n_full = min(wg_first / kPTile, n_t);   // tiles every row sees in full
 
-  const int row0 = wg_row0 + wave * 32;
-  const int rows_here = min(32, rows_b - row0);   // <= 0: idle wave (loads and barriers only)
+  const int row0 = wg_row0 + wave * 32 * RB;
+  const int rows_here = min(32 * RB, rows_b - row0);   // <= 0: idle wave
   const int wave_bound =
       rows_here > 0 ? row_key_bound(row0 + rows_here - 1, group, si.q_len, si.K_b, p.causal) : 0;
-  const int first_bound =
-      rows_here > 0 ? row_key_bound(row0, group, si.q_len, si.K_b, p.causal) : 0;
-  const int my_row = row0 + n32;
-  const bool row_ok = n32 < rows_here;
-  const int tok = row_ok ? my_row / group : 0;
-  const int h = g * group + (row_ok ? my_row - tok * group : 0);
-  const int row_lim = row_ok ? row_key_bound(my_row, group, si.q_len, si.K_b, p.causal) : 0;
+  bool row_ok[RB];
+  int tok[RB], hq_[RB], row_lim[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = row0 + rb * 32 + n32;
+    row_ok[rb] = rb * 32 + n32 < rows_here;
+    tok[rb] = row_ok[rb] ? r / group : 0;
+    hq_[rb] = g * group + (row_ok[rb] ? r - tok[rb] * group : 0);
+    row_lim[rb] = row_ok[rb] ? row_key_bound(r, group, si.q_len, si.K_b, p.causal) : 0;
+  }
 
-  u32x4 qf[QS];
-  {
-    const uint16_t *qrow = p.q + ((long)(si.cu_b + tok) * p.hq + h) * D;
+  u32x4 qf[RB][QS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const uint16_t *qrow = p.q + ((long)(si.cu_b + tok[rb]) * p.hq + hq_[rb]) * D;
 #pragma unroll
     for (int ds = 0; ds < QS; ++ds)
-      qf[ds] = row_ok ? load16(qrow + ds * 16 + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+      qf[rb][ds] = row_ok[rb] ? load16(qrow + ds * 16 + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
   }
 
   const CacheGeom &cg = p.geom;
@@ -636,7 +654,20 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
                           : Slab{(uint32_t)cg.contig_alloc * p.hkv * D * 2,
                                  (long)cg.contig_alloc * p.hkv * D};
   // Tile loads: instruction r of wave w fetches whole rows of keys
-  // t*64 + (w*64 + r*256)/CPR + lane/CPR (64*16/(2D) keys, one page).
+  // t*32 + (w*64 + r*256)/CPR + lane/CPR (64*16/(2D) keys, inside one page).
+  // The lane part of each byte offset is loop-invariant; the tile's first
+  // row inside its page goes in the uniform offset.
+  const uint32_t row_bytes = (uint32_t)p.hkv * D * 2;
+  const int in_page_mask = paged ? min((1 << shift), kPTile) - 1 : kPTile - 1;
+  uint32_t lane_off[NCH];
+  int lane_key[NCH];
+#pragma unroll
+  for (int r = 0; r < NCH; ++r) {
+    const int c = tid + r * kThreads;
+    lane_key[r] = c / CPR;
+    lane_off[r] = (uint32_t)(lane_key[r] & in_page_mask) * row_bytes +
+                  (uint32_t)(g * D + (c % CPR) * 8) * 2;
+  }
   // Page ids of tile t: lane r < NCH reads the entry of instruction r.
   auto load_ids = [&](int t) -> int {
     const int key = t * kPTile + (wave * 64 + (lane % NCH) * kThreads) / CPR;
@@ -646,160 +677,214 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   };
   u32x4 kst[NCH], vst[NCH];
   auto gload = [&](int t, int ids) {
+    const int key0 = t * kPTile;
+    const uint32_t uni = (uint32_t)(paged ? (key0 & ((1 << shift) - 1)) : key0) * row_bytes;
+    const int limit = paged ? wg_bound : min(wg_bound, cg.contig_alloc);
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
-      const int c = tid + r * kThreads;
-      const int key = t * kPTile + c / CPR;
-      const int col = c % CPR;
       int page = paged ? __builtin_amdgcn_readlane(ids, r) : b;
       const bool page_ok = !paged || (unsigned)page < (unsigned)cg.num_pages;
       page = page_ok ? page : 0;
-      const int slot = paged ? (key & ((1 << shift) - 1)) : key;
-      const bool ok = page_ok && key < wg_bound && (paged || key < cg.contig_alloc);
-      const uint32_t off = ok ? (uint32_t)(((slot * p.hkv + g) * D + col * 8) * 2) : kOOB;
-      kst[r] = buf_load16(page_rsrc(p.k_cache + page * slab.elems, slab.bytes), off);
-      vst[r] = buf_load16(page_rsrc(p.v_cache + page * slab.elems, slab.bytes), off);
+      const bool ok = page_ok && key0 + lane_key[r] < limit;
+      const uint32_t off = ok ? lane_off[r] : kOOB;
+      kst[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          page_rsrc(p.k_cache + page * slab.elems, slab.bytes), (int)off, (int)uni, 0));
+      vst[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          page_rsrc(p.v_cache + page * slab.elems, slab.bytes), (int)off, (int)uni, 0));
     }
   };
-  auto lstore = [&](int buf) {
-    uint16_t *kb = smem + buf * 2 * TILE_H;
-    uint16_t *vb = kb + TILE_H;
+  // LDS rings: K slots 0-1, V slots 0-2
+  auto kslot = [&](int t) { return smem + (t & 1) * KSLOT; };
+  auto vslot = [&](int t) { return smem + 2 * KSLOT + (t % 3) * VSLOT; };
+  auto lstore = [&](int t) {
+    uint16_t *kb = kslot(t);
+    uint16_t *vb = vslot(t);
 #pragma unroll
     for (int r = 0; r < NCH; ++r) {
       const int c = tid + r * kThreads;
-      const int off = (c / CPR) * KSTR + (c % CPR) * 8;
-      store16(kb + off, kst[r]);
-      store16(vb + off, vst[r]);
+      store16(kb + (c / CPR) * KSTR + (c % CPR) * 8, kst[r]);
+      store16(vb + (c / CPR) * VSTR + (c % CPR) * 8, vst[r]);
     }
   };
 
-  f32x16 o_acc[DBP];
-#pragma unroll
-  for (int db = 0; db < DBP; ++db) o_acc[db] = f32x16{};
-  float m_run = kNegInf;
-  float l_part = 0.f;
+  // operand read bases (lane part; the rest are immediate offsets)
+  const int k_base = n32 * KSTR + 8 * hh;
+  const int G = lane >> 4;
+  const int s16 = lane & 15;
+  const int v_base = (4 * (G >> 1) + (s16 >> 2)) * VSTR + 16 * (G & 1) + 4 * (s16 & 3);
 
-  // Loads are unconditional (tiles past the end read nothing); the only wait
-  // for global data is before staging the next tile, after this one's math.
+  // S^T blocks of one tile: sc[rb], key m of rows rb*32 + n32
+  auto qk = [&](int t, f32x16 (&sc)[RB]) {
+    const uint16_t *kt = kslot(t) + k_base;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sc[rb] = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < QS; ++ds) {
+      const u32x4 a = load16(kt + ds * 16);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sc[rb] = Elt<DT>::mfma32(a, qf[rb][ds], sc[rb]);
+    }
+  };
+
+  f32x16 o_acc[DBP][RB];
+#pragma unroll
+  for (int db = 0; db < DBP; ++db)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) o_acc[db][rb] = f32x16{};
+  float m_run[RB], l_part[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = kNegInf;   // reference maximum of raw scores (possibly stale by < 2^8)
+    l_part[rb] = 0.f;
+  }
+  const float c2 = p.scale_log2;
+
+  // softmax of tile t's scores and the PV product with its V tile.  Lane
+  // (n32, hh) element i of sc[rb] is key t*32 + (i/4)*8 + 4*hh + i%4.
+  auto softmax_pv = [&](int t, f32x16 (&sc)[RB], bool masked) {
+    float alpha[RB], m_sc[RB];
+    bool moved = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float tmax = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (masked) {
+          const int key = t * kPTile + (i >> 2) * 8 + 4 * hh + (i & 3);
+          sc[rb][i] = key < row_lim[rb] ? sc[rb][i] : kNegInf;
+        }
+        tmax = fmaxf(tmax, sc[rb][i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      // move the reference only when the maximum grew by more than 2^8
+      const bool move = (tmax - m_run[rb]) * c2 > kRescaleThreshold;
+      const float m_ref = move ? tmax : m_run[rb];
+      alpha[rb] = move ? fast_exp2((m_run[rb] - m_ref) * c2) : 1.f;
+      moved |= move;
+      m_run[rb] = m_ref;
+      m_sc[rb] = m_ref == kNegInf ? 0.f : m_ref * c2;
+    }
+    // P^T operands: k-step ks (16 keys) takes elements ks*8 .. ks*8+7
+    u32x4 pb[RB][2], pb_lo[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float psum = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(__builtin_fmaf(sc[rb][ks * 8 + 2 * e], c2, -m_sc[rb]));
+          const float p1 = fast_exp2(__builtin_fmaf(sc[rb][ks * 8 + 2 * e + 1], c2, -m_sc[rb]));
+          psum += p0 + p1;
+          pb[rb][ks][e] = pack2<DT>(p0, p1);
+          if constexpr (DT == kBF16) {
+            pb_lo[rb][ks][e] = pack2<DT>(p0 - Elt<DT>::to_f32((uint16_t)(pb[rb][ks][e] & 0xffffu)),
+                                         p1 - Elt<DT>::to_f32((uint16_t)(pb[rb][ks][e] >> 16)));
+          }
+        }
+      }
+      l_part[rb] = l_part[rb] * alpha[rb] + psum;
+    }
+    if (__any(moved)) {
+#pragma unroll
+      for (int db = 0; db < DBP; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o_acc[db][rb] *= alpha[rb];
+    }
+    // PV: lane group G reads dims db*32 + 16*(G&1) + 0..15, keys of k half G>>1
+    const uint16_t *vt = vslot(t) + v_base;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int db = 0; db < DBP; ++db) {
+        const u32x2 a0 = lds_read_tr16(vt + ks * 16 * VSTR + db * 32);
+        const u32x2 a1 = lds_read_tr16(vt + (ks * 16 + 8) * VSTR + db * 32);
+        const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          o_acc[db][rb] = Elt<DT>::mfma32(va, pb[rb][ks], o_acc[db][rb]);
+          if constexpr (DT == kBF16) o_acc[db][rb] = Elt<DT>::mfma32(va, pb_lo[rb][ks], o_acc[db][rb]);
+        }
+      }
+    }
+  };
+
+  // prologue: tiles 0 and 1 into LDS, S^T of tile 0
+  f32x16 s_a[RB], s_b[RB];
   int ids_next = 0;
   if (n_t > 0) {
     const int ids0 = load_ids(0);
+    const int ids1 = load_ids(1);
     gload(0, ids0);
-    ids_next = load_ids(1);
     lstore(0);
+    gload(1, ids1);
+    ids_next = load_ids(2);
+    lstore(1);
   }
   __syncthreads();
-  for (int t = 0; t < n_t; ++t) {
-    const int buf = t & 1;
-    const int ids_after = load_ids(t + 2);
-    gload(t + 1, ids_next);
-    if (t * kPTile < wave_bound) {
-      const uint16_t *kt = smem + buf * 2 * TILE_H;
-      const uint16_t *vt = kt + TILE_H;
-      f32x16 sc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sc[kb] = f32x16{};
-        const uint16_t *krow = kt + (kb * 32 + n32) * KSTR + 8 * hh;
-#pragma unroll
-        for (int ds = 0; ds < QS; ++ds)
-          sc[kb] = Elt<DT>::mfma32(load16(krow + ds * 16), qf[ds], sc[kb]);
-      }
-      // scale, mask, running max.  Lane (n32, hh) element i of block kb is key
-      // t*64 + kb*32 + (i/4)*8 + 4*hh + i%4 of row n32.
-      const bool full = (t + 1) * kPTile <= first_bound;
-      float tmax = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float v = sc[kb][i] * p.scale_log2;
-          if (!full) {
-            const int key = t * kPTile + kb * 32 + (i >> 2) * 8 + 4 * hh + (i & 3);
-            v = key < row_lim ? v : kNegInf;
-          }
-          sc[kb][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_use);
-      float psum = 0.f;
-      u32x4 pb[4], pb_lo[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(sc[ks >> 1][(ks & 1) * 8 + 2 * e] - m_use);
-          const float p1 = fast_exp2(sc[ks >> 1][(ks & 1) * 8 + 2 * e + 1] - m_use);
-          psum += p0 + p1;
-          pb[ks][e] = pack2<DT>(p0, p1);
-          if constexpr (DT == kBF16) {
-            pb_lo[ks][e] = pack2<DT>(p0 - Elt<DT>::to_f32((uint16_t)(pb[ks][e] & 0xffffu)),
-                                     p1 - Elt<DT>::to_f32((uint16_t)(pb[ks][e] >> 16)));
-          }
-        }
-      }
-      l_part = l_part * alpha + psum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DBP; ++db) o_acc[db] *= alpha;
-      }
-      // PV: lane group G reads dims db*32 + 16*(G&1) + 0..15, keys of k half G>>1
-      const int G = lane >> 4;
-      const int s16 = lane & 15;
-      const uint16_t *vtr = vt + (4 * (G >> 1) + (s16 >> 2)) * KSTR + 16 * (G & 1) + 4 * (s16 & 3);
-#pragma unroll
-      for (int db = 0; db < DBP; ++db) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const u32x2 a0 = lds_read_tr16(vtr + (ks * 16) * KSTR + db * 32);
-          const u32x2 a1 = lds_read_tr16(vtr + (ks * 16 + 8) * KSTR + db * 32);
-          const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]};
-          o_acc[db] = Elt<DT>::mfma32(va, pb[ks], o_acc[db]);
-          if constexpr (DT == kBF16) o_acc[db] = Elt<DT>::mfma32(va, pb_lo[ks], o_acc[db]);
-        }
-      }
+  if (n_t > 0) qk(0, s_a);
+
+  // iteration t: loads of tile t+2 in flight, QK^T of tile t+1 beside the
+  // softmax and PV of tile t, then tile t+2 into the slots freed by t.
+  // Full tiles: every wave computes, no mask.  Tail tiles: waves whose rows
+  // see nothing of a tile skip it.
+  auto iter = [&](int t, f32x16 (&cur)[RB], f32x16 (&nxt)[RB], bool tail) {
+    const int ids_after = load_ids(t + 3);
+    gload(t + 2, ids_next);
+    if (!tail) {
+      qk(t + 1, nxt);
+      softmax_pv(t, cur, false);
+    } else {
+      if ((t + 1) * kPTile < wave_bound) qk(t + 1, nxt);
+      if (t * kPTile < wave_bound) softmax_pv(t, cur, true);
     }
-    lstore(buf ^ 1);
+    lstore(t + 2);
     __syncthreads();
     ids_next = ids_after;
+  };
+  // the branch-free loop takes an even number of full tiles so the masked
+  // tail always starts on the same score registers
+  const int n_main = n_full & ~1;
+  int t = 0;
+  for (; t < n_main; t += 2) {
+    iter(t, s_a, s_b, false);
+    iter(t + 1, s_b, s_a, false);
+  }
+  for (; t < n_t; t += 2) {
+    iter(t, s_a, s_b, true);
+    if (t + 1 < n_t) iter(t + 1, s_b, s_a, true);
   }
 
-  if (!row_ok) return;
-  const float L = l_part + __shfl_xor(l_part, 32, 64);
-  const bool empty = !(L > 0.f);
-  const float inv = empty ? 0.f : 1.f / L;
-  const long ridx = (long)(si.cu_b + tok) * p.hq + h;
-  uint16_t *dst = p.out + ridx * D;
 #pragma unroll
-  for (int db = 0; db < DBP; ++db) {
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!row_ok[rb]) continue;
+    const float L = l_part[rb] + __shfl_xor(l_part[rb], 32, 64);
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : 1.f / L;
+    const long ridx = (long)(si.cu_b + tok[rb]) * p.hq + hq_[rb];
+    uint16_t *dst = p.out + ridx * D;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      u32x2 pk;
-      pk[0] = pack2<DT>(o_acc[db][q4 * 4 + 0] * inv, o_acc[db][q4 * 4 + 1] * inv);
-      pk[1] = pack2<DT>(o_acc[db][q4 * 4 + 2] * inv, o_acc[db][q4 * 4 + 3] * inv);
-      *reinterpret_cast<u32x2 *>(dst + db * 32 + q4 * 8 + 4 * hh) = pk;
+    for (int db = 0; db < DBP; ++db) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u32x2 pk;
+        pk[0] = pack2<DT>(o_acc[db][rb][q4 * 4 + 0] * inv, o_acc[db][rb][q4 * 4 + 1] * inv);
+        pk[1] = pack2<DT>(o_acc[db][rb][q4 * 4 + 2] * inv, o_acc[db][rb][q4 * 4 + 3] * inv);
+        *reinterpret_cast<u32x2 *>(dst + db * 32 + q4 * 8 + 4 * hh) = pk;
+      }
     }
+    if (hh == 0) p.lse[ridx] = empty ? kNegInf : (m_run[rb] * c2 + __builtin_log2f(L)) * kLn2;
   }
-  if (hh == 0) p.lse[ridx] = empty ? kNegInf : (m_run + __builtin_log2f(L)) * kLn2;
 }
 
-// ---------------------------------------------------------------------------
-// Unified attention kernel: one workgroup = one work unit.  Decode units and
-// prefill units of any mix of sequences share the grid; each workgroup finds
-// its unit from the device metadata (see locate_unit) and runs the matching
-// path.  Key tiles (32 keys in decode, 64 in prefill) and split boundaries
-// depend only on lengths, never on the page size or on which physical pages
-// hold the keys, so results are bit-identical across page sizes and page
-// relabellings.
-// ---------------------------------------------------------------------------
-template <int DT, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kPTile * (D + 8)];
+template <int DT, int D, bool kUnified>
+__device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
+  // decode units: 4 waves x (K + V tile of 32 rows); prefill units: K ring of
+  // two and V ring of three 32-row tiles
+  constexpr int kDecodeLds = kWaves * 2 * kKeyTile * D;
+  constexpr int kPrefillLds = 2 * kPTile * (D + 8) + 3 * kPTile * (D + 32);
+  __shared__ __attribute__((aligned(16)))
+  uint16_t smem[kUnified && kPrefillLds > kDecodeLds ? kPrefillLds : kDecodeLds];
   __shared__ float sm_m[kWaves][kDecodeRows];
   __shared__ float sm_l[kWaves][kDecodeRows];
   __shared__ int s_wsum[kWaves];
@@ -819,14 +904,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const SeqInfo si = seq_info(p, u.b);
   const int rows_b = si.q_len * p.group;
   if (rows_b <= 0) return;
-  if (p.all_decode || rows_b <= kDecodeRows) {
+  if (!kUnified || p.all_decode || rows_b <= kDecodeRows) {
     if (g == 0 && u.off == 0 && p.split_count != nullptr && threadIdx.x == 0)
       p.split_count[u.b] = u.splits;
     decode_unit<DT, D>(p, u.b, g, u.off, u.splits, si, smem, sm_m, sm_l);
-  } else {
+  } else if constexpr (kUnified) {
     const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
     prefill_unit<DT, D>(p, u.b, g, n_qt - 1 - u.off, si, smem);
   }
+}
+
+// Decode-only batches (every sequence fits a decode unit, known on the host):
+// two waves per SIMD.
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_decode_kernel(FwdParams p) {
+  attn_fwd_body<DT, D, false>(p);
+}
+
+// Unified kernel for any mix of prefill and decode sequences: two waves per
+// SIMD as well.
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdParams p) {
+  attn_fwd_body<DT, D, true>(p);
 }
 
 // ---------------------------------------------------------------------------
