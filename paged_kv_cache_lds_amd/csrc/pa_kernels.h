@@ -264,6 +264,73 @@ __device__ inline u32x2 lds_read_tr16(const uint16_t *p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// The eight LDS slots of a workgroup, one 32-row [key][D] tile each.  They
+// are separate LDS objects so that the compiler can tell a slot being filled
+// by LDS-destination loads from one being read, and keep those loads in
+// flight across the reads.
+constexpr int kSlots = 8;
+struct LdsPool {
+  uint16_t *s0, *s1, *s2, *s3, *s4, *s5, *s6, *s7;
+  // slot i for a constant i
+  __device__ uint16_t *s(int i) const {
+    return i < 4 ? (i < 2 ? (i == 0 ? s0 : s1) : (i == 2 ? s2 : s3))
+                 : (i < 6 ? (i == 4 ? s4 : s5) : (i == 6 ? s6 : s7));
+  }
+  // slot i for a run-time i.  The empty asm makes the candidates opaque, so
+  // the selection stays a few scalar selects instead of becoming a table of
+  // LDS addresses (which a static initializer cannot hold).
+  __device__ uint16_t *pick(int i) const {
+    typedef __attribute__((address_space(3))) uint16_t lds_u16;
+    lds_u16 *a0 = (lds_u16 *)s0, *a1 = (lds_u16 *)s1, *a2 = (lds_u16 *)s2, *a3 = (lds_u16 *)s3;
+    lds_u16 *a4 = (lds_u16 *)s4, *a5 = (lds_u16 *)s5, *a6 = (lds_u16 *)s6, *a7 = (lds_u16 *)s7;
+    asm volatile("" : "+s"(a0), "+s"(a1), "+s"(a2), "+s"(a3), "+s"(a4), "+s"(a5), "+s"(a6),
+                      "+s"(a7));
+    lds_u16 *r = i < 4 ? (i < 2 ? (i == 0 ? a0 : a1) : (i == 2 ? a2 : a3))
+                       : (i < 6 ? (i == 4 ? a4 : a5) : (i == 6 ? a6 : a7));
+    return (uint16_t *)r;   // still known to be LDS to the address-space inference
+  }
+};
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Where a decode unit stages wave w's K and V tiles (and, at the end, its
+// fp32 output rows in the K tile).  One contiguous array when the kernel runs
+// decode units only: the V tile is the K tile plus a constant, which keeps
+// the operand addresses in few registers.  The eight-slot pool when decode
+// and prefill units share a kernel.
+template <int TILEH>
+struct ContigDecodeLds {
+  uint16_t *base;
+  __device__ uint16_t *k(int w) const { return base + w * 2 * TILEH; }
+  __device__ uint16_t *v(int w) const { return k(w) + TILEH; }
+  __device__ uint16_t *k_const(int w) const { return k(w); }
+};
+struct PoolDecodeLds {
+  LdsPool pool;
+  __device__ uint16_t *k(int w) const { return pool.pick(2 * w); }
+  __device__ uint16_t *v(int w) const { return pool.pick(2 * w + 1); }
+  __device__ uint16_t *k_const(int w) const { return pool.s(2 * w); }
+};
+
+// s_waitcnt immediate (gfx9 fields): vmcnt (bits 3:0 and 15:14), expcnt 7 (no
+// wait, bits 6:4), lgkmcnt (bits 11:8).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+// All but the newest `VM` of this wave's loads (LDS-destination loads
+// included; loads complete in issue order) and all its LDS operations
+// complete, then a workgroup barrier: afterwards every wave sees whatever any
+// wave loaded into LDS before those VM, and no wave still reads a slot that is
+// about to be refilled.  The signal fences keep the compiler from moving
+// memory accesses across the barrier.
+template <int VM>
+__device__ inline void wait_then_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------------------
 // Decode unit: <= 16 packed rows (the G q heads of one kv head for one or a
 // few tokens), one split of the sequence's keys.  The four waves share the
@@ -289,10 +356,10 @@ __device__ inline u32x2 lds_read_tr16(const uint16_t *p) {
 //   O^T += V^T P^T 16x16x32 MFMA on key-contiguous V^T from transposing reads.
 // The waves' (max, sum, O) states merge through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int DT, int D>
+template <int DT, int D, class Lds>
 __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, const int g,
                                             const int split, const int S_b, const SeqInfo si,
-                                            uint16_t *smem, float (*sm_m)[kDecodeRows],
+                                            const Lds &lds, float (*sm_m)[kDecodeRows],
                                             float (*sm_l)[kDecodeRows]) {
   constexpr int DS = D / 32;       // k-steps of S^T (32 dims each)
   constexpr int DB = D / 16;       // 16-dim blocks of O^T
@@ -300,12 +367,11 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
   constexpr int KPI = 64 / CPR;    // keys per row-load instruction
   constexpr int NLD = kKeyTile / KPI;
   constexpr int ROWH = D;          // halves per staged row (no padding: swizzled)
-  constexpr int TILEH = kKeyTile * ROWH;
-  constexpr int REGION = 2 * TILEH;                // K tile, then V tile
-  static_assert(REGION * 2 >= kDecodeRows * D * 4, "wave region must hold its O staging");
+  constexpr int TILEH = kKeyTile * ROWH;          // halves per staged tile (one LDS slot)
+  static_assert(TILEH * 2 >= kDecodeRows * D * 4, "a K slot must hold the wave's O staging");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int lr = lane & 15;
   const int lg = lane >> 4;
   const int group = p.group;
@@ -353,7 +419,8 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
   // read is unconditional; lanes with nothing to read load a harmless word.
   auto load_ids = [&](int t) -> int {
     const int key = t * kKeyTile + (lane % NLD) * KPI;
-    const bool ok = paged && lane < NLD && key < key_end_w && (key >> shift) < cg.mpp;
+    // bitwise conditions and one unconditional load: no branch around it
+    const bool ok = paged & (lane < NLD) & (key < key_end_w) & ((key >> shift) < cg.mpp);
     const int32_t *src = ok ? cg.table + (long)b * cg.mpp + (key >> shift) : p.cu_seqlens_q;
     return *src;
   };
@@ -375,8 +442,10 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
     // the tile's one or two pages: those of the first load instruction and of
     // the first instruction of the tile's upper half (keys 16.., which start a
     // new page only when pages hold 16 keys)
-    int pg_a = paged ? __builtin_amdgcn_readlane(ids, 0) : b;
-    int pg_b = paged ? __builtin_amdgcn_readlane(ids, upper_lane) : b;
+    const int rl_a = __builtin_amdgcn_readlane(ids, 0);
+    const int rl_b = __builtin_amdgcn_readlane(ids, upper_lane);
+    int pg_a = paged ? rl_a : b;
+    int pg_b = paged ? rl_b : b;
     const bool ok_a = !paged || (unsigned)pg_a < (unsigned)cg.num_pages;
     const bool ok_b = !paged || (unsigned)pg_b < (unsigned)cg.num_pages;
     pg_a = ok_a ? pg_a : 0;
@@ -401,8 +470,8 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
   f32x4 o_acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint16_t *ks_ = smem + wave * REGION;   // K tile [32][D], chunk-swizzled rows
-  uint16_t *vs_ = ks_ + TILEH;            // V tile [32][D], chunk-swizzled rows
+  uint16_t *ks_ = lds.k(wave);   // K tile [32][D], chunk-swizzled rows
+  uint16_t *vs_ = lds.v(wave);   // V tile [32][D], chunk-swizzled rows
   // element offset of (key, 16-byte chunk) in a swizzled tile
   auto soff = [&](int key, int chunk) { return key * ROWH + ((chunk ^ (key & (CPR - 1))) << 3); };
 
@@ -540,7 +609,7 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
     for (int w = 0; w < kWaves; ++w) {
       const float wt = fast_exp2(sm_m[w][orow] - M);   // 0 for waves that saw nothing
       L += wt * sm_l[w][orow];
-      const float *src = reinterpret_cast<const float *>(smem + w * REGION) + orow * D + oc * CH;
+      const float *src = reinterpret_cast<const float *>(lds.k_const(w)) + orow * D + oc * CH;
 #pragma unroll
       for (int c = 0; c < CH; ++c) acc[c] += wt * src[c];
     }
@@ -578,40 +647,47 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
 
 // ---------------------------------------------------------------------------
 // Prefill unit: 128 packed rows (32 per wave) of one sequence and kv head,
-// every key those rows can see, one split.  32-key K and V tiles are
-// gathered page by page by the whole workgroup (unconditional buffer loads,
-// page ids fetched a tile ahead) into LDS rings - two K slots, three V slots,
-// one barrier per tile - and each iteration overlaps two tiles in every wave:
-//   S^T(t+1) = K Q^T   32x32x16 MFMA (keys on M)
-//   softmax(t)         online, log2 units, one fma + exp2 per score
-//   O^T += V^T P^T(t)  32x32x16 MFMA, V^T from transposing LDS reads
-// Tiles every row of the workgroup sees in full run in a branch-free main
-// loop (mask-free, so the next tile's MFMAs and this tile's VALU share one
-// basic block); the tiles on the causal diagonal follow in a masked tail.
-// The running maximum is only moved when it grows by more than 2^8 (the
-// stale maximum stays an exact common reference for the sum and the
-// accumulator, and probabilities stay <= 256), so rescaling is rare.  LDS
-// rows are padded (K: D+8, V: D+32 halves) so every operand read is a lane
-// base plus an immediate offset and conflict-free.
+// every key those rows can see, one split, in 32-key tiles:
+//   loads        each wave moves its share of a tile's K and V rows from the
+//                page straight into LDS (buffer loads with an LDS destination:
+//                lane l of an instruction fills bytes 16 l .. 16 l + 15 of one
+//                1 KiB block, and the lane chooses which 16-byte chunk of which
+//                row it fetches, so the swizzles below are free); keys past the
+//                visible range and pages outside the pool load as zeros; page
+//                ids are fetched one tile ahead by absolute logical index;
+//   LDS          two K slots and two V slots, separate LDS objects; K rows keep
+//                chunk c at c ^ (row & 7), V rows at c ^ 2 (row & 3), which
+//                makes both the 32x32 MFMA K reads and the transposing V reads
+//                bank-conflict free with every read a lane base plus an
+//                immediate offset; one barrier per tile;
+//   iteration t  K of tile t+2 and V of tile t+1 stream in while each wave
+//                computes S^T(t+1) = K Q^T (32x32x16 MFMA, keys on M) beside
+//                the online softmax of tile t (log2 units, one fma + exp2 per
+//                score) and O^T += V^T P^T(t) (32x32x16 MFMA, V^T from
+//                transposing LDS reads).
+// Tiles every row of the unit sees in full run in a branch-free, mask-free
+// loop; the tiles on the causal diagonal follow in a masked loop.  The running
+// maximum only moves when it grows by more than 2^8: the stale maximum stays
+// an exact common reference for the row sum and the accumulator, and
+// probabilities stay <= 256, so rescaling is rare.
 // ---------------------------------------------------------------------------
 constexpr float kRescaleThreshold = 8.f;   // log2 units
 
 template <int DT, int D>
 __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, const int g,
-                                             const int qtile, const SeqInfo si, uint16_t *smem) {
+                                             const int qtile, const SeqInfo si,
+                                             const LdsPool &pool) {
   constexpr int QS = D / 16;        // k-steps over D (16 dims each)
   constexpr int DBP = D / 32;       // 32-dim blocks of O^T
   constexpr int RB = kPrefillRB;    // 32-row blocks per wave
   constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int NCH = kPTile * CPR / kThreads;
-  constexpr int KSTR = D + 8;       // padded LDS row strides (halves)
-  constexpr int VSTR = D + 32;
-  constexpr int KSLOT = kPTile * KSTR;
-  constexpr int VSLOT = kPTile * VSTR;
-  static_assert(NCH * kThreads == kPTile * CPR, "tile chunks must divide the workgroup");
+  constexpr int RPB = 64 / CPR;     // rows per 1 KiB load block (4 or 8)
+  constexpr int NI = kPTile / (kWaves * RPB);   // load instructions per wave, tile and matrix
+  static_assert(NI >= 1 && NI * kWaves * RPB == kPTile, "a tile must split into load blocks");
+  static_assert(RPB == 4 || RPB == 8, "swizzle bookkeeping assumes 4 or 8 rows per block");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int n32 = lane & 31;       // MFMA column (row within a 32-row block)
   const int hh = lane >> 5;        // k half
   const int group = p.group;
@@ -647,80 +723,88 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
       qf[rb][ds] = row_ok[rb] ? load16(qrow + ds * 16 + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
   }
 
+  // ---- loads ----
+  // Instruction r of wave w fills block bb = r * 4 + w of a slot: rows
+  // bb * RPB + lane / CPR, physical chunk lane % CPR, i.e. the logical chunk
+  // that the row's swizzle puts there.  bb * RPB is a multiple of 4 (of 8 when
+  // RPB is 8, or when RPB is 4 and w is even), so both swizzles are fixed per
+  // lane and the lane part of every byte offset is loop-invariant.
   const CacheGeom &cg = p.geom;
   const bool paged = cg.table != nullptr;
   const int shift = cg.page_shift;
-  const Slab slab = paged ? Slab{(uint32_t)(p.hkv * D * 2) << shift, (long)(p.hkv * D) << shift}
-                          : Slab{(uint32_t)cg.contig_alloc * p.hkv * D * 2,
-                                 (long)cg.contig_alloc * p.hkv * D};
-  // Tile loads: instruction r of wave w fetches whole rows of keys
-  // t*32 + (w*64 + r*256)/CPR + lane/CPR (64*16/(2D) keys, inside one page).
-  // The lane part of each byte offset is loop-invariant; the tile's first
-  // row inside its page goes in the uniform offset.
   const uint32_t row_bytes = (uint32_t)p.hkv * D * 2;
-  const int in_page_mask = paged ? min((1 << shift), kPTile) - 1 : kPTile - 1;
-  uint32_t lane_off[NCH];
-  int lane_key[NCH];
-#pragma unroll
-  for (int r = 0; r < NCH; ++r) {
-    const int c = tid + r * kThreads;
-    lane_key[r] = c / CPR;
-    lane_off[r] = (uint32_t)(lane_key[r] & in_page_mask) * row_bytes +
-                  (uint32_t)(g * D + (c % CPR) * 8) * 2;
-  }
-  // Page ids of tile t: lane r < NCH reads the entry of instruction r.
+  const uint32_t slab_bytes = paged ? row_bytes << shift : (uint32_t)cg.contig_alloc * row_bytes;
+  const int limit = paged ? wg_bound : min(wg_bound, cg.contig_alloc);
+  const int lrow = lane / CPR;
+  const int pch = lane % CPR;
+  const int krow7 = ((RPB == 4 ? 4 * (wave & 1) : 0) + lrow) & 7;
+  const uint32_t k_lane = (uint32_t)lrow * row_bytes + (uint32_t)(g * D + ((pch ^ krow7) << 3)) * 2;
+  const uint32_t v_lane =
+      (uint32_t)lrow * row_bytes + (uint32_t)(g * D + ((pch ^ ((lrow & 3) << 1)) << 3)) * 2;
+  // page ids of tile t: lane r < NI reads the page of this wave's instruction r
   auto load_ids = [&](int t) -> int {
-    const int key = t * kPTile + (wave * 64 + (lane % NCH) * kThreads) / CPR;
-    const bool ok = paged && lane < NCH && key < wg_bound && (key >> shift) < cg.mpp;
+    const int key = t * kPTile + ((lane % NI) * kWaves + wave) * RPB;
+    // bitwise conditions and one unconditional load: no branch around it
+    const bool ok = paged & (lane < NI) & (key < wg_bound) & ((key >> shift) < cg.mpp);
     const int32_t *src = ok ? cg.table + (long)b * cg.mpp + (key >> shift) : p.cu_seqlens_q;
     return *src;
   };
-  u32x4 kst[NCH], vst[NCH];
-  auto gload = [&](int t, int ids) {
-    const int key0 = t * kPTile;
-    const uint32_t uni = (uint32_t)(paged ? (key0 & ((1 << shift) - 1)) : key0) * row_bytes;
-    const int limit = paged ? wg_bound : min(wg_bound, cg.contig_alloc);
+  // one matrix (K or V) of tile t into an LDS slot.  The page arithmetic runs
+  // across lanes (lane r < NI: instruction r's page): byte address of the page
+  // and the descriptor's record count - the slab size, or 0 for a page outside
+  // the pool, whose loads then all read zeros; each load takes them with three
+  // lane reads.
+  const uint32_t pmask = paged ? (1u << shift) - 1u : 0xffffffffu;
+  auto load_tile = [&](const uint16_t *cache, uint16_t *slot, uint32_t lane_part, int t, int ids) {
+    const uint32_t page = paged ? (uint32_t)ids : (uint32_t)b;
+    const bool page_ok = !paged | (page < (uint32_t)cg.num_pages);
+    const uint64_t addr = (uint64_t)(uintptr_t)cache + (uint64_t)page * slab_bytes;
+    const uint32_t a_lo = (uint32_t)addr;
+    const uint32_t a_hi = (uint32_t)(addr >> 32);
+    const uint32_t nrec = page_ok ? slab_bytes : 0u;
 #pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      int page = paged ? __builtin_amdgcn_readlane(ids, r) : b;
-      const bool page_ok = !paged || (unsigned)page < (unsigned)cg.num_pages;
-      page = page_ok ? page : 0;
-      const bool ok = page_ok && key0 + lane_key[r] < limit;
-      const uint32_t off = ok ? lane_off[r] : kOOB;
-      kst[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          page_rsrc(p.k_cache + page * slab.elems, slab.bytes), (int)off, (int)uni, 0));
-      vst[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          page_rsrc(p.v_cache + page * slab.elems, slab.bytes), (int)off, (int)uni, 0));
+    for (int r = 0; r < NI; ++r) {
+      const int bb = r * kWaves + wave;
+      const int key0 = t * kPTile + bb * RPB;   // first row of the block (wave-uniform)
+      const uint32_t lo = __builtin_amdgcn_readlane(a_lo, r);
+      const uint32_t hi = __builtin_amdgcn_readlane(a_hi, r);
+      const uint32_t nr = __builtin_amdgcn_readlane(nrec, r);
+      const uint16_t *base = (const uint16_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+      // row of the block inside its slab, capped at the slab size so that an
+      // out-of-range lane offset cannot wrap back into range
+      const uint32_t uni = min(((uint32_t)key0 & pmask) * row_bytes, slab_bytes);
+      const bool ok = key0 + lrow < limit;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(base, nr), (lds_void *)(slot + bb * 512),
+                                               16, ok ? lane_part : kOOB, uni, 0, 0);
     }
   };
-  // LDS rings: K slots 0-1, V slots 0-2
-  auto kslot = [&](int t) { return smem + (t & 1) * KSLOT; };
-  auto vslot = [&](int t) { return smem + 2 * KSLOT + (t % 3) * VSLOT; };
-  auto lstore = [&](int t) {
-    uint16_t *kb = kslot(t);
-    uint16_t *vb = vslot(t);
-#pragma unroll
-    for (int r = 0; r < NCH; ++r) {
-      const int c = tid + r * kThreads;
-      store16(kb + (c / CPR) * KSTR + (c % CPR) * 8, kst[r]);
-      store16(vb + (c / CPR) * VSTR + (c % CPR) * 8, vst[r]);
-    }
-  };
+  // rings of four: K of tile t in slot t % 4, V of tile t in slot 4 + t % 4
+  uint16_t *const k_slot[4] = {pool.s0, pool.s1, pool.s2, pool.s3};
+  uint16_t *const v_slot[4] = {pool.s4, pool.s5, pool.s6, pool.s7};
 
-  // operand read bases (lane part; the rest are immediate offsets)
-  const int k_base = n32 * KSTR + 8 * hh;
+  // operand reads.  K: lane (n32, hh) reads logical chunk 2 ds + hh of row n32,
+  // stored at chunk (2 ds + hh) ^ (n32 & 7) = 8 (ds / 4) + ((2 (ds % 4) + hh) ^ (n32 & 7)).
+  int k_rd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) k_rd[i] = n32 * D + ((((2 * i + hh) ^ (n32 & 7)) & 7) << 3);
+  // V^T: lane s of 16-lane group G reads row 4 (G / 2) + s / 4 (+ 16 ks, + 8),
+  // dims 32 db + 16 (G & 1) + 4 (s % 4) .. + 3, i.e. logical chunk
+  // 4 db + 2 (G & 1) + (s % 4) / 2, stored at that chunk ^ 2 (s / 4).
   const int G = lane >> 4;
   const int s16 = lane & 15;
-  const int v_base = (4 * (G >> 1) + (s16 >> 2)) * VSTR + 16 * (G & 1) + 4 * (s16 & 3);
+  int v_rd[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    v_rd[e] = (4 * (G >> 1) + (s16 >> 2)) * D +
+              (((4 * e + 2 * (G & 1) + ((s16 & 3) >> 1)) ^ (2 * (s16 >> 2))) << 3) + 4 * (s16 & 1);
 
   // S^T blocks of one tile: sc[rb], key m of rows rb*32 + n32
-  auto qk = [&](int t, f32x16 (&sc)[RB]) {
-    const uint16_t *kt = kslot(t) + k_base;
+  auto qk = [&](const uint16_t *ks, f32x16 (&sc)[RB]) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) sc[rb] = f32x16{};
 #pragma unroll
     for (int ds = 0; ds < QS; ++ds) {
-      const u32x4 a = load16(kt + ds * 16);
+      const u32x4 a = load16(ks + k_rd[ds & 3] + (ds >> 2) * 64);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) sc[rb] = Elt<DT>::mfma32(a, qf[rb][ds], sc[rb]);
     }
@@ -741,7 +825,7 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
 
   // softmax of tile t's scores and the PV product with its V tile.  Lane
   // (n32, hh) element i of sc[rb] is key t*32 + (i/4)*8 + 4*hh + i%4.
-  auto softmax_pv = [&](int t, f32x16 (&sc)[RB], bool masked) {
+  auto softmax_pv = [&](int t, const uint16_t *vs, f32x16 (&sc)[RB], bool masked) {
     float alpha[RB], m_sc[RB];
     bool moved = false;
 #pragma unroll
@@ -792,13 +876,13 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
         for (int rb = 0; rb < RB; ++rb) o_acc[db][rb] *= alpha[rb];
     }
     // PV: lane group G reads dims db*32 + 16*(G&1) + 0..15, keys of k half G>>1
-    const uint16_t *vt = vslot(t) + v_base;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int db = 0; db < DBP; ++db) {
-        const u32x2 a0 = lds_read_tr16(vt + ks * 16 * VSTR + db * 32);
-        const u32x2 a1 = lds_read_tr16(vt + (ks * 16 + 8) * VSTR + db * 32);
+        const uint16_t *vt = vs + v_rd[db & 1] + (db >> 1) * 64 + ks * 16 * D;
+        const u32x2 a0 = lds_read_tr16(vt);
+        const u32x2 a1 = lds_read_tr16(vt + 8 * D);
         const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -809,50 +893,67 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     }
   };
 
-  // prologue: tiles 0 and 1 into LDS, S^T of tile 0
+  // prologue: K of tiles 0-3 and V of tiles 0-2 into LDS, S^T of tile 0; the
+  // second barrier lets every wave finish reading K(0) before its slot is
+  // refilled.  Loads past the bound are zeros, so nothing here is conditional.
   f32x16 s_a[RB], s_b[RB];
-  int ids_next = 0;
-  if (n_t > 0) {
-    const int ids0 = load_ids(0);
-    const int ids1 = load_ids(1);
-    gload(0, ids0);
-    lstore(0);
-    gload(1, ids1);
-    ids_next = load_ids(2);
-    lstore(1);
+  int ids_v, ids_k;   // page ids of tiles t+3 and t+4 at the start of iteration t
+  {
+    const int ids_0 = load_ids(0);
+    const int ids_1 = load_ids(1);
+    const int ids_2 = load_ids(2);
+    ids_v = load_ids(3);
+    ids_k = load_ids(4);
+    load_tile(p.k_cache, k_slot[0], k_lane, 0, ids_0);
+    load_tile(p.v_cache, v_slot[0], v_lane, 0, ids_0);
+    load_tile(p.k_cache, k_slot[1], k_lane, 1, ids_1);
+    load_tile(p.v_cache, v_slot[1], v_lane, 1, ids_1);
+    load_tile(p.k_cache, k_slot[2], k_lane, 2, ids_2);
+    load_tile(p.v_cache, v_slot[2], v_lane, 2, ids_2);
+    load_tile(p.k_cache, k_slot[3], k_lane, 3, ids_v);
   }
-  __syncthreads();
-  if (n_t > 0) qk(0, s_a);
+  wait_then_barrier<0>();
+  qk(k_slot[0], s_a);
+  wait_then_barrier<0>();
 
-  // iteration t: loads of tile t+2 in flight, QK^T of tile t+1 beside the
-  // softmax and PV of tile t, then tile t+2 into the slots freed by t.
-  // Full tiles: every wave computes, no mask.  Tail tiles: waves whose rows
-  // see nothing of a tile skip it.
-  auto iter = [&](int t, f32x16 (&cur)[RB], f32x16 (&nxt)[RB], bool tail) {
-    const int ids_after = load_ids(t + 3);
-    gload(t + 2, ids_next);
+  // iteration t (ph = t % 4): page ids of tile t+5, then K(t+4) into the slot
+  // K(t) used and V(t+3) into the slot V(t-1) used; QK^T of tile t+1 beside
+  // the softmax and PV of tile t.  At the barrier the loads issued two
+  // iterations earlier - K(t+2) and V(t+1), read next iteration - must have
+  // landed; the newest two iterations' loads stay in flight.  Full tiles:
+  // every wave computes, no mask.  Tail tiles: waves whose rows see nothing of
+  // a tile skip it.
+  constexpr int kLoadsPerIter = 1 + 2 * NI;
+  auto iter = [&](int t, int ph, f32x16 (&cur)[RB], f32x16 (&nxt)[RB], bool tail) {
+    const int ids_new = load_ids(t + 5);
+    load_tile(p.k_cache, k_slot[ph], k_lane, t + 4, ids_k);
+    load_tile(p.v_cache, v_slot[(ph + 3) & 3], v_lane, t + 3, ids_v);
     if (!tail) {
-      qk(t + 1, nxt);
-      softmax_pv(t, cur, false);
+      qk(k_slot[(ph + 1) & 3], nxt);
+      softmax_pv(t, v_slot[ph], cur, false);
     } else {
-      if ((t + 1) * kPTile < wave_bound) qk(t + 1, nxt);
-      if (t * kPTile < wave_bound) softmax_pv(t, cur, true);
+      if ((t + 1) * kPTile < wave_bound) qk(k_slot[(ph + 1) & 3], nxt);
+      if (t * kPTile < wave_bound) softmax_pv(t, v_slot[ph], cur, true);
     }
-    lstore(t + 2);
-    __syncthreads();
-    ids_next = ids_after;
+    wait_then_barrier<2 * kLoadsPerIter>();
+    ids_v = ids_k;
+    ids_k = ids_new;
   };
-  // the branch-free loop takes an even number of full tiles so the masked
-  // tail always starts on the same score registers
-  const int n_main = n_full & ~1;
+  // the branch-free loop takes a multiple of four full tiles, so every slot
+  // index is a constant and the masked tail starts on the same registers
+  const int n_main = n_full & ~3;
   int t = 0;
-  for (; t < n_main; t += 2) {
-    iter(t, s_a, s_b, false);
-    iter(t + 1, s_b, s_a, false);
+  for (; t < n_main; t += 4) {
+    iter(t, 0, s_a, s_b, false);
+    iter(t + 1, 1, s_b, s_a, false);
+    iter(t + 2, 2, s_a, s_b, false);
+    iter(t + 3, 3, s_b, s_a, false);
   }
-  for (; t < n_t; t += 2) {
-    iter(t, s_a, s_b, true);
-    if (t + 1 < n_t) iter(t + 1, s_b, s_a, true);
+  for (; t < n_t; t += 4) {
+    iter(t, 0, s_a, s_b, true);
+    if (t + 1 < n_t) iter(t + 1, 1, s_b, s_a, true);
+    if (t + 2 < n_t) iter(t + 2, 2, s_a, s_b, true);
+    if (t + 3 < n_t) iter(t + 3, 3, s_b, s_a, true);
   }
 
 #pragma unroll
@@ -879,12 +980,20 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
 
 template <int DT, int D, bool kUnified>
 __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
-  // decode units: 4 waves x (K + V tile of 32 rows); prefill units: K ring of
-  // two and V ring of three 32-row tiles
-  constexpr int kDecodeLds = kWaves * 2 * kKeyTile * D;
-  constexpr int kPrefillLds = 2 * kPTile * (D + 8) + 3 * kPTile * (D + 32);
-  __shared__ __attribute__((aligned(16)))
-  uint16_t smem[kUnified && kPrefillLds > kDecodeLds ? kPrefillLds : kDecodeLds];
+  // decode-only kernel: one contiguous array, a K and a V tile per wave;
+  // unified kernel: eight separate 32-row slots (four K and four V slots of a
+  // prefill unit; a K/V pair per wave of a decode unit)
+  constexpr int kSlotH = kKeyTile * D;
+  static_assert(kPTile == kKeyTile, "prefill and decode tiles share the slots");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s0[kUnified ? kSlotH : kSlots * kSlotH];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s1[kUnified ? kSlotH : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s2[kUnified ? kSlotH : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s3[kUnified ? kSlotH : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s4[kUnified ? kSlotH : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s5[kUnified ? kSlotH : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s6[kUnified ? kSlotH : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s7[kUnified ? kSlotH : 8];
+  const LdsPool pool{lds_s0, lds_s1, lds_s2, lds_s3, lds_s4, lds_s5, lds_s6, lds_s7};
   __shared__ float sm_m[kWaves][kDecodeRows];
   __shared__ float sm_l[kWaves][kDecodeRows];
   __shared__ int s_wsum[kWaves];
@@ -901,16 +1010,28 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   } else if (!locate_unit(p, unit, u, s_wsum, s_found)) {
     return;
   }
-  const SeqInfo si = seq_info(p, u.b);
+  // the unit and its sequence are the same for every lane: keep them in SGPRs
+  // (page indices, buffer descriptors and uniform offsets derive from them)
+  u.b = __builtin_amdgcn_readfirstlane(u.b);
+  u.off = __builtin_amdgcn_readfirstlane(u.off);
+  u.splits = __builtin_amdgcn_readfirstlane(u.splits);
+  SeqInfo si = seq_info(p, u.b);
+  si.cu_b = __builtin_amdgcn_readfirstlane(si.cu_b);
+  si.q_len = __builtin_amdgcn_readfirstlane(si.q_len);
+  si.K_b = __builtin_amdgcn_readfirstlane(si.K_b);
   const int rows_b = si.q_len * p.group;
   if (rows_b <= 0) return;
   if (!kUnified || p.all_decode || rows_b <= kDecodeRows) {
     if (g == 0 && u.off == 0 && p.split_count != nullptr && threadIdx.x == 0)
       p.split_count[u.b] = u.splits;
-    decode_unit<DT, D>(p, u.b, g, u.off, u.splits, si, smem, sm_m, sm_l);
+    if constexpr (kUnified)
+      decode_unit<DT, D>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds{pool}, sm_m, sm_l);
+    else
+      decode_unit<DT, D>(p, u.b, g, u.off, u.splits, si, ContigDecodeLds<kSlotH>{lds_s0}, sm_m,
+                         sm_l);
   } else if constexpr (kUnified) {
     const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
-    prefill_unit<DT, D>(p, u.b, g, n_qt - 1 - u.off, si, smem);
+    prefill_unit<DT, D>(p, u.b, g, n_qt - 1 - u.off, si, pool);
   }
 }
 
