@@ -673,6 +673,21 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
 // ---------------------------------------------------------------------------
 constexpr float kRescaleThreshold = 8.f;   // log2 units
 
+// acc + x.lo + x.hi for two packed 16-bit floats (one dot-product instruction
+// against (1, 1); the products are exact, the sum is fp32)
+template <int DT>
+__device__ inline float add_pair(uint32_t x, float acc) {
+  if constexpr (DT == kF16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, x), h2{(_Float16)1.f, (_Float16)1.f}, acc,
+                                  false);
+  } else {
+    typedef short s2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s2, x), s2{0x3f80, 0x3f80}, acc,
+                                           false);
+  }
+}
+
 template <int DT, int D>
 __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, const int g,
                                              const int qtile, const SeqInfo si,
@@ -723,12 +738,24 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
       qf[rb][ds] = row_ok[rb] ? load16(qrow + ds * 16 + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
   }
 
+  // ---- LDS layout ----
+  // LDS serves 256 bytes a clock in 64 four-byte banks: 16 lanes of a 16-byte
+  // read, or 32 lanes of an 8-byte read, at a time.  Rows of 2 D bytes all
+  // start on the same bank (D = 128) or on one of two (D = 64), so chunks are
+  // XOR-swizzled per row:
+  //   K, D = 128: chunk c at c ^ (row & 7), and the 1 KiB blocks of rows 8-15
+  //               and 24-31 sit 128 bytes later - the 16 rows one 16-byte MFMA
+  //               read touches fall on 16 different bank groups;
+  //   K, D = 64:  chunk c at c ^ ((row / 2) & 7), same effect;
+  //   V:          the 64-byte segment of chunk c moves by the row, c ^ 4 (row & 3)
+  //               (D = 128) or c ^ 4 ((row / 2) & 1) (D = 64), so the four rows
+  //               one transposing read touches fall on four different quarters.
   // ---- loads ----
   // Instruction r of wave w fills block bb = r * 4 + w of a slot: rows
   // bb * RPB + lane / CPR, physical chunk lane % CPR, i.e. the logical chunk
-  // that the row's swizzle puts there.  bb * RPB is a multiple of 4 (of 8 when
-  // RPB is 8, or when RPB is 4 and w is even), so both swizzles are fixed per
-  // lane and the lane part of every byte offset is loop-invariant.
+  // that the row's swizzle puts there.  bb * RPB is a multiple of 4, and of 8
+  // when RPB is 8 or w is even, so the swizzles are fixed per lane and the
+  // lane part of every byte offset is loop-invariant.
   const CacheGeom &cg = p.geom;
   const bool paged = cg.table != nullptr;
   const int shift = cg.page_shift;
@@ -737,10 +764,15 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   const int limit = paged ? wg_bound : min(wg_bound, cg.contig_alloc);
   const int lrow = lane / CPR;
   const int pch = lane % CPR;
-  const int krow7 = ((RPB == 4 ? 4 * (wave & 1) : 0) + lrow) & 7;
-  const uint32_t k_lane = (uint32_t)lrow * row_bytes + (uint32_t)(g * D + ((pch ^ krow7) << 3)) * 2;
-  const uint32_t v_lane =
-      (uint32_t)lrow * row_bytes + (uint32_t)(g * D + ((pch ^ ((lrow & 3) << 1)) << 3)) * 2;
+  // row & 7 (D = 128) or (row / 2) & 7 (D = 64) of this lane's row, and the
+  // V segment swizzle of that row
+  const int kx = D == 128 ? ((4 * (wave & 1) + lrow) & 7) : ((4 * wave + (lrow >> 1)) & 7);
+  const int vx = D == 128 ? ((lrow & 3) << 2) : (((lrow >> 1) & 1) << 2);
+  const uint32_t k_lane = (uint32_t)lrow * row_bytes + (uint32_t)(g * D + ((pch ^ kx) << 3)) * 2;
+  const uint32_t v_lane = (uint32_t)lrow * row_bytes + (uint32_t)(g * D + ((pch ^ vx) << 3)) * 2;
+  // halves from a slot's start to block bb (K slots carry the D = 128 padding)
+  auto k_block = [](int bb) { return bb * 512 + (D == 128 ? 64 * (bb >> 1) : 0); };
+  auto v_block = [](int bb) { return bb * 512; };
   // page ids of tile t: lane r < NI reads the page of this wave's instruction r
   auto load_ids = [&](int t) -> int {
     const int key = t * kPTile + ((lane % NI) * kWaves + wave) * RPB;
@@ -755,7 +787,8 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   // the pool, whose loads then all read zeros; each load takes them with three
   // lane reads.
   const uint32_t pmask = paged ? (1u << shift) - 1u : 0xffffffffu;
-  auto load_tile = [&](const uint16_t *cache, uint16_t *slot, uint32_t lane_part, int t, int ids) {
+  auto load_tile = [&](const uint16_t *cache, uint16_t *slot, uint32_t lane_part, auto block,
+                       int t, int ids) {
     const uint32_t page = paged ? (uint32_t)ids : (uint32_t)b;
     const bool page_ok = !paged | (page < (uint32_t)cg.num_pages);
     const uint64_t addr = (uint64_t)(uintptr_t)cache + (uint64_t)page * slab_bytes;
@@ -774,7 +807,7 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
       // out-of-range lane offset cannot wrap back into range
       const uint32_t uni = min(((uint32_t)key0 & pmask) * row_bytes, slab_bytes);
       const bool ok = key0 + lrow < limit;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(base, nr), (lds_void *)(slot + bb * 512),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(base, nr), (lds_void *)(slot + block(bb)),
                                                16, ok ? lane_part : kOOB, uni, 0, 0);
     }
   };
@@ -782,21 +815,30 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   uint16_t *const k_slot[4] = {pool.s0, pool.s1, pool.s2, pool.s3};
   uint16_t *const v_slot[4] = {pool.s4, pool.s5, pool.s6, pool.s7};
 
-  // operand reads.  K: lane (n32, hh) reads logical chunk 2 ds + hh of row n32,
-  // stored at chunk (2 ds + hh) ^ (n32 & 7) = 8 (ds / 4) + ((2 (ds % 4) + hh) ^ (n32 & 7)).
+  // operand reads.  K: lane (n32, hh) reads logical chunk 2 ds + hh of row n32;
+  // with ds = 4 j + i that is stored at 8 j + ((2 i + hh) ^ x), x the row's
+  // swizzle, so four lane bases and immediate offsets cover every ds.
   int k_rd[4];
+  {
+    const int x = D == 128 ? (n32 & 7) : ((n32 >> 1) & 7);
+    const int row_base = n32 * D + (D == 128 ? 64 * (n32 >> 3) : 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) k_rd[i] = n32 * D + ((((2 * i + hh) ^ (n32 & 7)) & 7) << 3);
+    for (int i = 0; i < 4; ++i) k_rd[i] = row_base + (((2 * i + hh) ^ x) << 3);
+  }
   // V^T: lane s of 16-lane group G reads row 4 (G / 2) + s / 4 (+ 16 ks, + 8),
   // dims 32 db + 16 (G & 1) + 4 (s % 4) .. + 3, i.e. logical chunk
-  // 4 db + 2 (G & 1) + (s % 4) / 2, stored at that chunk ^ 2 (s / 4).
+  // 4 db + 2 (G & 1) + (s % 4) / 2; its segment db is stored at db ^ y, y the
+  // row's segment swizzle (+ 16 and + 8 rows keep it).
   const int G = lane >> 4;
   const int s16 = lane & 15;
-  int v_rd[2];
+  int v_rd[DBP];
+  {
+    const int y = D == 128 ? (s16 >> 2) : ((s16 >> 3) & 1);
 #pragma unroll
-  for (int e = 0; e < 2; ++e)
-    v_rd[e] = (4 * (G >> 1) + (s16 >> 2)) * D +
-              (((4 * e + 2 * (G & 1) + ((s16 & 3) >> 1)) ^ (2 * (s16 >> 2))) << 3) + 4 * (s16 & 1);
+    for (int db = 0; db < DBP; ++db)
+      v_rd[db] = (4 * (G >> 1) + (s16 >> 2)) * D +
+                 ((4 * (db ^ y) + 2 * (G & 1) + ((s16 & 3) >> 1)) << 3) + 4 * (s16 & 1);
+  }
 
   // S^T blocks of one tile: sc[rb], key m of rows rb*32 + n32
   auto qk = [&](const uint16_t *ks, f32x16 (&sc)[RB]) {
@@ -823,10 +865,23 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   }
   const float c2 = p.scale_log2;
 
-  // softmax of tile t's scores and the PV product with its V tile.  Lane
-  // (n32, hh) element i of sc[rb] is key t*32 + (i/4)*8 + 4*hh + i%4.
-  auto softmax_pv = [&](int t, const uint16_t *vs, f32x16 (&sc)[RB], bool masked) {
-    float alpha[RB], m_sc[RB];
+  float m_sc[RB];   // m_run * c2, 0 for an empty reference
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) m_sc[rb] = 0.f;
+
+  // The online softmax is split around the MFMA work.  tile_max(t) runs as
+  // soon as tile t's scores exist (beside the PV product of the previous
+  // tile): mask, row maximum, and - when the maximum grew by more than 2^8 -
+  // a new reference, with the row sum and the accumulator rescaled to it.
+  // exp_pv(t) then runs one iteration later beside the next tile's QK^T:
+  // probabilities against the reference, row sums, O^T += V^T P^T.
+  // The row sums add the probabilities as rounded for the PV product (so a
+  // constant V comes back exactly), and each tile's sum is pinned to its
+  // iteration: left alone, the compiler defers the sums of a whole unrolled
+  // group to the loop latch and keeps every probability live until then.
+  // Lane (n32, hh) element i of sc[rb] is key t*32 + (i/4)*8 + 4*hh + i%4.
+  auto tile_max = [&](int t, f32x16 (&sc)[RB], bool masked) {
+    float alpha[RB];
     bool moved = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -840,34 +895,13 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
         tmax = fmaxf(tmax, sc[rb][i]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      // move the reference only when the maximum grew by more than 2^8
       const bool move = (tmax - m_run[rb]) * c2 > kRescaleThreshold;
       const float m_ref = move ? tmax : m_run[rb];
       alpha[rb] = move ? fast_exp2((m_run[rb] - m_ref) * c2) : 1.f;
       moved |= move;
       m_run[rb] = m_ref;
       m_sc[rb] = m_ref == kNegInf ? 0.f : m_ref * c2;
-    }
-    // P^T operands: k-step ks (16 keys) takes elements ks*8 .. ks*8+7
-    u32x4 pb[RB][2], pb_lo[RB][2];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float psum = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(__builtin_fmaf(sc[rb][ks * 8 + 2 * e], c2, -m_sc[rb]));
-          const float p1 = fast_exp2(__builtin_fmaf(sc[rb][ks * 8 + 2 * e + 1], c2, -m_sc[rb]));
-          psum += p0 + p1;
-          pb[rb][ks][e] = pack2<DT>(p0, p1);
-          if constexpr (DT == kBF16) {
-            pb_lo[rb][ks][e] = pack2<DT>(p0 - Elt<DT>::to_f32((uint16_t)(pb[rb][ks][e] & 0xffffu)),
-                                         p1 - Elt<DT>::to_f32((uint16_t)(pb[rb][ks][e] >> 16)));
-          }
-        }
-      }
-      l_part[rb] = l_part[rb] * alpha[rb] + psum;
+      l_part[rb] *= alpha[rb];
     }
     if (__any(moved)) {
 #pragma unroll
@@ -875,12 +909,37 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) o_acc[db][rb] *= alpha[rb];
     }
+  };
+  auto exp_pv = [&](const uint16_t *vs, const f32x16 (&sc)[RB]) {
+    // P^T operands: k-step ks (16 keys) takes elements ks*8 .. ks*8+7
+    u32x4 pb[RB][2], pb_lo[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float l = l_part[rb];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(__builtin_fmaf(sc[rb][ks * 8 + 2 * e], c2, -m_sc[rb]));
+          const float p1 = fast_exp2(__builtin_fmaf(sc[rb][ks * 8 + 2 * e + 1], c2, -m_sc[rb]));
+          pb[rb][ks][e] = pack2<DT>(p0, p1);
+          l = add_pair<DT>(pb[rb][ks][e], l);
+          if constexpr (DT == kBF16) {
+            pb_lo[rb][ks][e] = pack2<DT>(p0 - Elt<DT>::to_f32((uint16_t)(pb[rb][ks][e] & 0xffffu)),
+                                         p1 - Elt<DT>::to_f32((uint16_t)(pb[rb][ks][e] >> 16)));
+            l = add_pair<DT>(pb_lo[rb][ks][e], l);
+          }
+        }
+      }
+      asm volatile("" : "+v"(l));
+      l_part[rb] = l;
+    }
     // PV: lane group G reads dims db*32 + 16*(G&1) + 0..15, keys of k half G>>1
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int db = 0; db < DBP; ++db) {
-        const uint16_t *vt = vs + v_rd[db & 1] + (db >> 1) * 64 + ks * 16 * D;
+        const uint16_t *vt = vs + v_rd[db] + ks * 16 * D;
         const u32x2 a0 = lds_read_tr16(vt);
         const u32x2 a1 = lds_read_tr16(vt + 8 * D);
         const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]};
@@ -904,44 +963,50 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     const int ids_2 = load_ids(2);
     ids_v = load_ids(3);
     ids_k = load_ids(4);
-    load_tile(p.k_cache, k_slot[0], k_lane, 0, ids_0);
-    load_tile(p.v_cache, v_slot[0], v_lane, 0, ids_0);
-    load_tile(p.k_cache, k_slot[1], k_lane, 1, ids_1);
-    load_tile(p.v_cache, v_slot[1], v_lane, 1, ids_1);
-    load_tile(p.k_cache, k_slot[2], k_lane, 2, ids_2);
-    load_tile(p.v_cache, v_slot[2], v_lane, 2, ids_2);
-    load_tile(p.k_cache, k_slot[3], k_lane, 3, ids_v);
+    load_tile(p.k_cache, k_slot[0], k_lane, k_block, 0, ids_0);
+    load_tile(p.v_cache, v_slot[0], v_lane, v_block, 0, ids_0);
+    load_tile(p.k_cache, k_slot[1], k_lane, k_block, 1, ids_1);
+    load_tile(p.v_cache, v_slot[1], v_lane, v_block, 1, ids_1);
+    load_tile(p.k_cache, k_slot[2], k_lane, k_block, 2, ids_2);
+    load_tile(p.v_cache, v_slot[2], v_lane, v_block, 2, ids_2);
+    load_tile(p.k_cache, k_slot[3], k_lane, k_block, 3, ids_v);
   }
   wait_then_barrier<0>();
   qk(k_slot[0], s_a);
+  tile_max(0, s_a, n_full == 0);
   wait_then_barrier<0>();
 
   // iteration t (ph = t % 4): page ids of tile t+5, then K(t+4) into the slot
   // K(t) used and V(t+3) into the slot V(t-1) used; QK^T of tile t+1 beside
-  // the softmax and PV of tile t.  At the barrier the loads issued two
-  // iterations earlier - K(t+2) and V(t+1), read next iteration - must have
-  // landed; the newest two iterations' loads stay in flight.  Full tiles:
-  // every wave computes, no mask.  Tail tiles: waves whose rows see nothing of
-  // a tile skip it.
+  // the probabilities of tile t, the PV product of tile t, and tile t+1's
+  // maximum beside that.  At the barrier the loads issued two iterations
+  // earlier - K(t+2) and V(t+1), read next iteration - must have landed; the
+  // newest two iterations' loads stay in flight.  Full tiles: every wave
+  // computes, no mask, and no branch before the rare rescale.  Tail tiles:
+  // waves whose rows see nothing of a tile skip it.
   constexpr int kLoadsPerIter = 1 + 2 * NI;
   auto iter = [&](int t, int ph, f32x16 (&cur)[RB], f32x16 (&nxt)[RB], bool tail) {
     const int ids_new = load_ids(t + 5);
-    load_tile(p.k_cache, k_slot[ph], k_lane, t + 4, ids_k);
-    load_tile(p.v_cache, v_slot[(ph + 3) & 3], v_lane, t + 3, ids_v);
+    load_tile(p.k_cache, k_slot[ph], k_lane, k_block, t + 4, ids_k);
+    load_tile(p.v_cache, v_slot[(ph + 3) & 3], v_lane, v_block, t + 3, ids_v);
     if (!tail) {
       qk(k_slot[(ph + 1) & 3], nxt);
-      softmax_pv(t, v_slot[ph], cur, false);
+      exp_pv(v_slot[ph], cur);
+      tile_max(t + 1, nxt, false);
     } else {
-      if ((t + 1) * kPTile < wave_bound) qk(k_slot[(ph + 1) & 3], nxt);
-      if (t * kPTile < wave_bound) softmax_pv(t, v_slot[ph], cur, true);
+      const bool next_seen = (t + 1) * kPTile < wave_bound;
+      if (next_seen) qk(k_slot[(ph + 1) & 3], nxt);
+      if (t * kPTile < wave_bound) exp_pv(v_slot[ph], cur);
+      if (next_seen) tile_max(t + 1, nxt, true);
     }
     wait_then_barrier<2 * kLoadsPerIter>();
     ids_v = ids_k;
     ids_k = ids_new;
   };
-  // the branch-free loop takes a multiple of four full tiles, so every slot
-  // index is a constant and the masked tail starts on the same registers
-  const int n_main = n_full & ~3;
+  // the branch-free loop takes a multiple of four tiles whose successors are
+  // full as well (so its unmasked maxima are right), every slot index is a
+  // constant, and the masked loop starts on the same registers
+  const int n_main = max(n_full - 1, 0) & ~3;
   int t = 0;
   for (; t < n_main; t += 4) {
     iter(t, 0, s_a, s_b, false);
@@ -983,9 +1048,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   // decode-only kernel: one contiguous array, a K and a V tile per wave;
   // unified kernel: eight separate 32-row slots (four K and four V slots of a
   // prefill unit; a K/V pair per wave of a decode unit)
-  constexpr int kSlotH = kKeyTile * D;
+  // (K slots of a prefill unit at D = 128 carry 64 halves of padding per two
+  // 1 KiB blocks)
+  constexpr int kSlotH = kKeyTile * D + (D == 128 ? 4 * 64 : 0);
   static_assert(kPTile == kKeyTile, "prefill and decode tiles share the slots");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_s0[kUnified ? kSlotH : kSlots * kSlotH];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_s0[kUnified ? kSlotH : kSlots * kKeyTile * D];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_s1[kUnified ? kSlotH : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_s2[kUnified ? kSlotH : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_s3[kUnified ? kSlotH : 8];
@@ -1027,7 +1094,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     if constexpr (kUnified)
       decode_unit<DT, D>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds{pool}, sm_m, sm_l);
     else
-      decode_unit<DT, D>(p, u.b, g, u.off, u.splits, si, ContigDecodeLds<kSlotH>{lds_s0}, sm_m,
+      decode_unit<DT, D>(p, u.b, g, u.off, u.splits, si, ContigDecodeLds<kKeyTile * D>{lds_s0}, sm_m,
                          sm_l);
   } else if constexpr (kUnified) {
     const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
