@@ -62,9 +62,18 @@ template <> struct Elt<kBF16> {
   }
 };
 
+// Two fp32 values rounded to nearest even and packed (lo in bits 0-15): one
+// packed-convert instruction on gfx950.
 template <int DT>
 __device__ inline uint32_t pack2(float lo, float hi) {
-  return (uint32_t)Elt<DT>::from_f32(lo) | ((uint32_t)Elt<DT>::from_f32(hi) << 16);
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  if constexpr (DT == kF16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, h2));
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, b2));
+  }
 }
 
 __device__ inline u32x4 load16(const uint16_t *p) {

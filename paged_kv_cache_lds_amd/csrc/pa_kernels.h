@@ -688,7 +688,7 @@ __device__ inline float add_pair(uint32_t x, float acc) {
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, bool kPaged>
 __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, const int g,
                                              const int qtile, const SeqInfo si,
                                              const LdsPool &pool) {
@@ -757,7 +757,7 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   // when RPB is 8 or w is even, so the swizzles are fixed per lane and the
   // lane part of every byte offset is loop-invariant.
   const CacheGeom &cg = p.geom;
-  const bool paged = cg.table != nullptr;
+  constexpr bool paged = kPaged;   // block table (else one contiguous allocation per sequence)
   const int shift = cg.page_shift;
   const uint32_t row_bytes = (uint32_t)p.hkv * D * 2;
   const uint32_t slab_bytes = paged ? row_bytes << shift : (uint32_t)cg.contig_alloc * row_bytes;
@@ -773,42 +773,69 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   // halves from a slot's start to block bb (K slots carry the D = 128 padding)
   auto k_block = [](int bb) { return bb * 512 + (D == 128 ? 64 * (bb >> 1) : 0); };
   auto v_block = [](int bb) { return bb * 512; };
-  // page ids of tile t: lane r < NI reads the page of this wave's instruction r
-  auto load_ids = [&](int t) -> int {
-    const int key = t * kPTile + ((lane % NI) * kWaves + wave) * RPB;
-    // bitwise conditions and one unconditional load: no branch around it
-    const bool ok = paged & (lane < NI) & (key < wg_bound) & ((key >> shift) < cg.mpp);
-    const int32_t *src = ok ? cg.table + (long)b * cg.mpp + (key >> shift) : p.cu_seqlens_q;
-    return *src;
+  // page ids of tile t, one per load instruction of this wave, read with
+  // wave-uniform loads through the constant address space (the table is
+  // read-only during the call), so they land in scalar registers.  The index
+  // is clamped to the last entry the unit may read; a block past that range
+  // loads nothing anyway (its lanes are out of range).
+  typedef __attribute__((address_space(4))) const int32_t c_i32;
+  struct PageIds {
+    int v[NI];
   };
-  // one matrix (K or V) of tile t into an LDS slot.  The page arithmetic runs
-  // across lanes (lane r < NI: instruction r's page): byte address of the page
-  // and the descriptor's record count - the slab size, or 0 for a page outside
-  // the pool, whose loads then all read zeros; each load takes them with three
-  // lane reads.
+  c_i32 *trow = nullptr;
+  int last_pg = 0;
+  if constexpr (kPaged) {
+    trow = (c_i32 *)(cg.table + (long)b * cg.mpp);
+    last_pg = max(0, min(cg.mpp, (wg_bound + (1 << shift) - 1) >> shift) - 1);
+  }
+  auto load_ids = [&](int t) -> PageIds {
+    PageIds ids;
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      if constexpr (kPaged)
+        ids.v[r] = trow[min((t * kPTile + (r * kWaves + wave) * RPB) >> shift, last_pg)];
+      else
+        ids.v[r] = b;
+    }
+    return ids;
+  };
+  // What a tile's loads need, kept in scalar registers from the K load of the
+  // tile to its V load one iteration later: per instruction, the page's byte
+  // offset in the pool, the descriptor's record count (the slab size, or 0
+  // for a page outside the pool, whose loads then all read zeros) and the
+  // block's first row inside the page (capped at the slab size so that an
+  // out-of-range lane offset cannot wrap back into range).
   const uint32_t pmask = paged ? (1u << shift) - 1u : 0xffffffffu;
+  struct TileInfo {
+    uint32_t off_lo[NI], off_hi[NI], nrec[NI], uni[NI];
+  };
+  auto tile_info = [&](int t, const PageIds &ids) -> TileInfo {
+    TileInfo ti;
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      const uint32_t pg = (uint32_t)ids.v[r];
+      const uint64_t off = (uint64_t)pg * slab_bytes;
+      ti.off_lo[r] = (uint32_t)off;
+      ti.off_hi[r] = (uint32_t)(off >> 32);
+      ti.nrec[r] = (!paged || pg < (uint32_t)cg.num_pages) ? slab_bytes : 0u;
+      const int key0 = t * kPTile + (r * kWaves + wave) * RPB;
+      ti.uni[r] = min(((uint32_t)key0 & pmask) * row_bytes, slab_bytes);
+    }
+    return ti;
+  };
+  // one matrix (K or V) of tile t into an LDS slot
   auto load_tile = [&](const uint16_t *cache, uint16_t *slot, uint32_t lane_part, auto block,
-                       int t, int ids) {
-    const uint32_t page = paged ? (uint32_t)ids : (uint32_t)b;
-    const bool page_ok = !paged | (page < (uint32_t)cg.num_pages);
-    const uint64_t addr = (uint64_t)(uintptr_t)cache + (uint64_t)page * slab_bytes;
-    const uint32_t a_lo = (uint32_t)addr;
-    const uint32_t a_hi = (uint32_t)(addr >> 32);
-    const uint32_t nrec = page_ok ? slab_bytes : 0u;
+                       int t, const TileInfo &ti) {
 #pragma unroll
     for (int r = 0; r < NI; ++r) {
       const int bb = r * kWaves + wave;
       const int key0 = t * kPTile + bb * RPB;   // first row of the block (wave-uniform)
-      const uint32_t lo = __builtin_amdgcn_readlane(a_lo, r);
-      const uint32_t hi = __builtin_amdgcn_readlane(a_hi, r);
-      const uint32_t nr = __builtin_amdgcn_readlane(nrec, r);
-      const uint16_t *base = (const uint16_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
-      // row of the block inside its slab, capped at the slab size so that an
-      // out-of-range lane offset cannot wrap back into range
-      const uint32_t uni = min(((uint32_t)key0 & pmask) * row_bytes, slab_bytes);
+      const uint16_t *base = (const uint16_t *)((uintptr_t)cache +
+                                                (((uint64_t)ti.off_hi[r] << 32) | ti.off_lo[r]));
       const bool ok = key0 + lrow < limit;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(base, nr), (lds_void *)(slot + block(bb)),
-                                               16, ok ? lane_part : kOOB, uni, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(base, ti.nrec[r]),
+                                               (lds_void *)(slot + block(bb)), 16,
+                                               ok ? lane_part : kOOB, ti.uni[r], 0, 0);
     }
   };
   // rings of four: K of tile t in slot t % 4, V of tile t in slot 4 + t % 4
@@ -956,20 +983,21 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   // second barrier lets every wave finish reading K(0) before its slot is
   // refilled.  Loads past the bound are zeros, so nothing here is conditional.
   f32x16 s_a[RB], s_b[RB];
-  int ids_v, ids_k;   // page ids of tiles t+3 and t+4 at the start of iteration t
+  TileInfo ti_v;    // loads of tile t+3 at the start of iteration t (its K is in flight)
+  PageIds ids_k;    // page ids of tile t+4
   {
-    const int ids_0 = load_ids(0);
-    const int ids_1 = load_ids(1);
-    const int ids_2 = load_ids(2);
-    ids_v = load_ids(3);
+    const TileInfo ti_0 = tile_info(0, load_ids(0));
+    const TileInfo ti_1 = tile_info(1, load_ids(1));
+    const TileInfo ti_2 = tile_info(2, load_ids(2));
+    ti_v = tile_info(3, load_ids(3));
     ids_k = load_ids(4);
-    load_tile(p.k_cache, k_slot[0], k_lane, k_block, 0, ids_0);
-    load_tile(p.v_cache, v_slot[0], v_lane, v_block, 0, ids_0);
-    load_tile(p.k_cache, k_slot[1], k_lane, k_block, 1, ids_1);
-    load_tile(p.v_cache, v_slot[1], v_lane, v_block, 1, ids_1);
-    load_tile(p.k_cache, k_slot[2], k_lane, k_block, 2, ids_2);
-    load_tile(p.v_cache, v_slot[2], v_lane, v_block, 2, ids_2);
-    load_tile(p.k_cache, k_slot[3], k_lane, k_block, 3, ids_v);
+    load_tile(p.k_cache, k_slot[0], k_lane, k_block, 0, ti_0);
+    load_tile(p.v_cache, v_slot[0], v_lane, v_block, 0, ti_0);
+    load_tile(p.k_cache, k_slot[1], k_lane, k_block, 1, ti_1);
+    load_tile(p.v_cache, v_slot[1], v_lane, v_block, 1, ti_1);
+    load_tile(p.k_cache, k_slot[2], k_lane, k_block, 2, ti_2);
+    load_tile(p.v_cache, v_slot[2], v_lane, v_block, 2, ti_2);
+    load_tile(p.k_cache, k_slot[3], k_lane, k_block, 3, ti_v);
   }
   wait_then_barrier<0>();
   qk(k_slot[0], s_a);
@@ -984,11 +1012,12 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   // newest two iterations' loads stay in flight.  Full tiles: every wave
   // computes, no mask, and no branch before the rare rescale.  Tail tiles:
   // waves whose rows see nothing of a tile skip it.
-  constexpr int kLoadsPerIter = 1 + 2 * NI;
+  constexpr int kLoadsPerIter = 2 * NI;   // vector loads (the page ids are scalar)
   auto iter = [&](int t, int ph, f32x16 (&cur)[RB], f32x16 (&nxt)[RB], bool tail) {
-    const int ids_new = load_ids(t + 5);
-    load_tile(p.k_cache, k_slot[ph], k_lane, k_block, t + 4, ids_k);
-    load_tile(p.v_cache, v_slot[(ph + 3) & 3], v_lane, v_block, t + 3, ids_v);
+    const PageIds ids_new = load_ids(t + 5);
+    const TileInfo ti_k = tile_info(t + 4, ids_k);
+    load_tile(p.k_cache, k_slot[ph], k_lane, k_block, t + 4, ti_k);
+    load_tile(p.v_cache, v_slot[(ph + 3) & 3], v_lane, v_block, t + 3, ti_v);
     if (!tail) {
       qk(k_slot[(ph + 1) & 3], nxt);
       exp_pv(v_slot[ph], cur);
@@ -1000,7 +1029,7 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
       if (next_seen) tile_max(t + 1, nxt, true);
     }
     wait_then_barrier<2 * kLoadsPerIter>();
-    ids_v = ids_k;
+    ti_v = ti_k;
     ids_k = ids_new;
   };
   // the branch-free loop takes a multiple of four tiles whose successors are
@@ -1098,7 +1127,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
                          sm_l);
   } else if constexpr (kUnified) {
     const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
-    prefill_unit<DT, D>(p, u.b, g, n_qt - 1 - u.off, si, pool);
+    if (p.geom.table != nullptr)
+      prefill_unit<DT, D, true>(p, u.b, g, n_qt - 1 - u.off, si, pool);
+    else
+      prefill_unit<DT, D, false>(p, u.b, g, n_qt - 1 - u.off, si, pool);
   }
 }
 
