@@ -66,7 +66,9 @@ def causal_flops(case):
     return 4 * case.head_dim * case.num_heads_q * total
 
 
-KERNEL_SOURCES = ("paged_kv_cache_lds_amd/csrc/pa_device.h", "paged_kv_cache_lds_amd/csrc/pa_kernels.h",
+# every source the decode kernel is built from (the prefill unit is not part of it)
+KERNEL_SOURCES = ("paged_kv_cache_lds_amd/csrc/pa_device.h", "paged_kv_cache_lds_amd/csrc/pa_common.h",
+                  "paged_kv_cache_lds_amd/csrc/pa_decode.h", "paged_kv_cache_lds_amd/csrc/pa_kernels.h",
                   "paged_kv_cache_lds_amd/csrc/paged_attn.hip")
 TRAFFIC_PROFILE = "profiles/attn_fwd_mha_decode_b256_ctx4096.txt"
 
@@ -338,7 +340,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(args.batch, args.ctx),
-                "kernel": "attn_fwd_kernel<f16,128>", "launch_ms": round(attn_ms, 4),
+                "kernel": "attn_decode_kernel<f16,128>", "launch_ms": round(attn_ms, 4),
                 "bytes_per_launch": attn_bytes, "splits": splits}
 
     # ---- CPU baseline: the oracle on a bounded sample of whole sequences ----

@@ -1,0 +1,330 @@
+// Shared pieces of the gfx950 paged KV-cache attention kernels: work
+// decomposition constants, kernel parameters, the KV append kernel,
+// sequence and unit bookkeeping, buffer-load and LDS helpers.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+
+// Work decomposition constants.
+constexpr int kThreads = 256;     // four wave64 per workgroup
+constexpr int kWaves = 4;
+constexpr int kKeyTile = 32;      // decode: keys per wave main-loop iteration
+constexpr int kDecodeRows = 16;   // packed (token, q-head) rows of a decode unit
+constexpr int kPrefillRB = 1;     // 32-row MFMA blocks per wave in a prefill unit
+constexpr int kPrefillRows = 32 * kPrefillRB * kWaves;   // rows of a prefill unit
+constexpr int kPTile = 32;        // prefill: keys per workgroup main-loop iteration
+constexpr int kMaxSplits = 128;
+constexpr int kWindow = 64;       // block-table entries a wave holds at once (one per lane)
+
+struct FwdParams {
+  const uint16_t *q;
+  const uint16_t *k_cache;
+  const uint16_t *v_cache;
+  CacheGeom geom;
+  const int32_t *cache_seqlens;
+  const int32_t *cu_seqlens_q;
+  uint16_t *out;
+  float *lse;
+  float *o_part;       // [max_splits, total_q, hq, D] fp32 (num_splits > 1)
+  float *lse_part;     // [max_splits, total_q, hq]
+  int32_t *split_count;// [batch]: splits given to each decode-mode sequence
+  int batch, total_q, hq, hkv, group;
+  int appended, causal, num_splits;
+  float scale_log2;    // softmax scale * log2(e)
+  int all_decode;      // host knows every sequence has q_len * group <= 16
+};
+
+struct AppendParams {
+  uint16_t *k_cache;
+  uint16_t *v_cache;
+  CacheGeom geom;
+  const int32_t *cache_seqlens;
+  const int32_t *cu_seqlens_q;
+  const uint16_t *k_new;
+  const uint16_t *v_new;
+  int batch, total_q, hkv, head_dim, tokens_per_block;
+};
+
+// ---------------------------------------------------------------------------
+// Append (vLLM's reshape_and_cache; the in-call k=/v= of flash-attention's
+// paged cache): new row i of sequence b goes to logical position
+// cache_seqlens[b] + i.  Grid (cdiv(max_seqlen_q, tokens_per_block), batch);
+// each thread moves 16-byte vectors.  Targets whose page id is outside the
+// pool (a caller precondition violation) are skipped, never written.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
+  const int b = blockIdx.y;
+  const int cu_b = p.cu_seqlens_q[b];
+  // rows past total_q (malformed cu_seqlens_q) are never touched
+  const int q_len = max(0, min(p.cu_seqlens_q[b + 1], p.total_q) - cu_b);
+  const int tok0 = blockIdx.x * p.tokens_per_block;
+  if (tok0 >= q_len) return;
+  const int ntok = min(p.tokens_per_block, q_len - tok0);
+  const int vec_per_row = p.hkv * p.head_dim / 8;   // 16-byte vectors per token row
+  const int L = p.cache_seqlens[b];
+  const int work = ntok * vec_per_row * 2;
+  for (int idx = threadIdx.x; idx < work; idx += kThreads) {
+    const int which = idx / (ntok * vec_per_row);     // 0: K, 1: V
+    const int rem = idx - which * ntok * vec_per_row;
+    const int t = rem / vec_per_row;
+    const int v = rem - t * vec_per_row;
+    const int i = tok0 + t;
+    const long prow = physical_row(p.geom, b, L + i);
+    if (prow < 0) continue;
+    const long src = ((long)(cu_b + i) * vec_per_row + v) * 8;
+    const long dst = (prow * vec_per_row + v) * 8;
+    if (which == 0) {
+      store16(p.k_cache + dst, load16(p.k_new + src));
+    } else {
+      store16(p.v_cache + dst, load16(p.v_new + src));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-sequence bookkeeping shared by every workgroup (and by the combine).
+// ---------------------------------------------------------------------------
+struct SeqInfo {
+  int cu_b, q_len, K_b;
+};
+
+__device__ inline SeqInfo seq_info(const FwdParams &p, int b) {
+  SeqInfo s;
+  s.cu_b = p.cu_seqlens_q[b];
+  s.q_len = max(0, min(p.cu_seqlens_q[b + 1], p.total_q) - s.cu_b);
+  s.K_b = max(0, p.cache_seqlens[b]) + (p.appended ? s.q_len : 0);
+  return s;
+}
+
+// Splits of a decode-mode sequence.  The host fixes the unit budget per kv
+// head (num_splits per decode sequence on average) from static sizes only;
+// here, with the real lengths in hand, every decode sequence keeps one unit
+// and the remaining budget is shared in proportion to its key tiles, so long
+// sequences get more splits than short ones (cache_seqlens never travels to
+// the host).  A pure function of the lengths: every workgroup agrees on it.
+__device__ inline int seq_splits(long extra_budget, long tiles_b, long total_tiles) {
+  if (extra_budget <= 0 || total_tiles <= 0) return 1;
+  const long s = 1 + (extra_budget * tiles_b) / total_tiles;
+  return (int)min(s, (long)kMaxSplits);
+}
+
+__device__ inline int decode_tiles(int K_b) { return (K_b + kKeyTile - 1) / kKeyTile; }
+
+// inclusive prefix sum over the workgroup (every thread contributes x);
+// `total` receives the workgroup sum
+__device__ inline int block_inclusive_scan(int x, int *s_wsum, int &total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wsum[wave] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int v = s_wsum[w];
+    before += (w < wave) ? v : 0;
+    total += v;
+  }
+  __syncthreads();
+  return before + x;
+}
+
+// Unified work mapping.  Units per kv head: a sequence whose packed rows
+// (q_len * group) fit one 16-row decode unit gets seq_splits() units (its
+// keys split across workgroups); a longer one gets cdiv(rows, 128) prefill
+// units, heaviest (last, under the causal mask) first.  The host sizes the
+// grid from static maxima; each workgroup finds its (sequence, unit) by
+// block-wide scans over the device metadata, and surplus workgroups return.
+struct UnitInfo {
+  int b, off, splits;   // off = split (decode) or query tile (prefill)
+};
+
+__device__ inline bool locate_unit(const FwdParams &p, int unit, UnitInfo &u, int *s_wsum,
+                                   int *s_found) {
+  const int tid = threadIdx.x;
+  const int S = p.num_splits;
+  // pass 1: decode-mode sequence count and their key tiles
+  long extra = 0, total_tiles = 0;
+  if (S > 1) {
+    long n_dec = 0, tiles = 0;
+    for (int c0 = 0; c0 < p.batch; c0 += kThreads) {
+      const int bb = c0 + tid;
+      int dec = 0, t = 0;
+      if (bb < p.batch) {
+        const SeqInfo si = seq_info(p, bb);
+        const int rows = si.q_len * p.group;
+        if (rows > 0 && (p.all_decode || rows <= kDecodeRows)) {
+          dec = 1;
+          t = decode_tiles(si.K_b);
+        }
+      }
+      int tot_d, tot_t;
+      block_inclusive_scan(dec, s_wsum, tot_d);
+      block_inclusive_scan(t, s_wsum, tot_t);
+      n_dec += tot_d;
+      tiles += tot_t;
+    }
+    extra = n_dec * (S - 1);
+    total_tiles = tiles;
+  }
+  // pass 2: prefix of units, find ours
+  if (tid == 0) s_found[0] = -1;
+  __syncthreads();
+  int carry = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += kThreads) {
+    const int bb = c0 + tid;
+    int units = 0, splits = 1;
+    if (bb < p.batch) {
+      const SeqInfo si = seq_info(p, bb);
+      const int rows = si.q_len * p.group;
+      if (rows > 0) {
+        if (p.all_decode || rows <= kDecodeRows) {
+          splits = seq_splits(extra, decode_tiles(si.K_b), total_tiles);
+          units = splits;
+        } else {
+          units = (rows + kPrefillRows - 1) / kPrefillRows;
+        }
+      }
+    }
+    int total;
+    const int incl = carry + block_inclusive_scan(units, s_wsum, total);
+    const int excl = incl - units;
+    if (units > 0 && unit >= excl && unit < incl) {
+      s_found[0] = bb;
+      s_found[1] = unit - excl;
+      s_found[2] = splits;
+    }
+    carry += total;
+    __syncthreads();
+    if (s_found[0] >= 0) break;
+  }
+  u.b = s_found[0];
+  u.off = s_found[1];
+  u.splits = s_found[2];
+  return u.b >= 0;
+}
+
+// keys visible to packed row r of a sequence (bottom-right causal alignment)
+__device__ inline int row_key_bound(int r, int group, int q_len, int K_b, int causal) {
+  if (!causal) return K_b;
+  const int lim = K_b - q_len + r / group + 1;
+  return max(0, min(lim, K_b));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer loads over one page (or one contiguous sequence) of the pool:
+// 32-bit per-lane byte offsets against a wave-uniform base, and any offset at
+// or past the range returns zeros without touching memory.  Masked lanes use
+// kOOB, so no load sits behind a branch and the compiler can count
+// outstanding loads exactly (keeping several tiles in flight).
+constexpr uint32_t kOOB = 0x80000000u;
+__device__ inline __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+// Streaming variant (nt: the rows are read once and should not displace
+// cached data): lane offset plus a wave-uniform offset.
+__device__ inline u32x4 buf_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t lane_off,
+                                          uint32_t uniform_off) {
+  return __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, (int)uniform_off, 2));
+}
+
+// Geometry of one "slab" the buffer loads address: a physical page in paged
+// mode, a sequence's whole allocation in contiguous mode.  A key's row within
+// the slab is key % page_size (paged) or key (contiguous).
+struct Slab {
+  uint32_t bytes;        // bytes per slab (host checks < 2^31)
+  long elems;            // halves per slab
+};
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i % 4 of the 8-byte rows addressed by lanes i / 4 + 4 j,
+// j = 0..3.  Lane s addressing row k0 + s / 4, columns c0 + 4 (s % 4) .. +3 of
+// a row-major [key][dim] tile therefore hands lane i the four keys k0 .. k0+3
+// of dim c0 + i: the key-contiguous operand layout the PV product needs.
+__device__ inline u32x2 lds_read_tr16(const uint16_t *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// The eight LDS slots of a workgroup, one 32-row [key][D] tile each.  They
+// are separate LDS objects so that the compiler can tell a slot being filled
+// by LDS-destination loads from one being read, and keep those loads in
+// flight across the reads.
+constexpr int kSlots = 8;
+struct LdsPool {
+  uint16_t *s0, *s1, *s2, *s3, *s4, *s5, *s6, *s7;
+  // slot i for a constant i
+  __device__ uint16_t *s(int i) const {
+    return i < 4 ? (i < 2 ? (i == 0 ? s0 : s1) : (i == 2 ? s2 : s3))
+                 : (i < 6 ? (i == 4 ? s4 : s5) : (i == 6 ? s6 : s7));
+  }
+  // slot i for a run-time i.  The empty asm makes the candidates opaque, so
+  // the selection stays a few scalar selects instead of becoming a table of
+  // LDS addresses (which a static initializer cannot hold).
+  __device__ uint16_t *pick(int i) const {
+    typedef __attribute__((address_space(3))) uint16_t lds_u16;
+    lds_u16 *a0 = (lds_u16 *)s0, *a1 = (lds_u16 *)s1, *a2 = (lds_u16 *)s2, *a3 = (lds_u16 *)s3;
+    lds_u16 *a4 = (lds_u16 *)s4, *a5 = (lds_u16 *)s5, *a6 = (lds_u16 *)s6, *a7 = (lds_u16 *)s7;
+    asm volatile("" : "+s"(a0), "+s"(a1), "+s"(a2), "+s"(a3), "+s"(a4), "+s"(a5), "+s"(a6),
+                      "+s"(a7));
+    lds_u16 *r = i < 4 ? (i < 2 ? (i == 0 ? a0 : a1) : (i == 2 ? a2 : a3))
+                       : (i < 6 ? (i == 4 ? a4 : a5) : (i == 6 ? a6 : a7));
+    return (uint16_t *)r;   // still known to be LDS to the address-space inference
+  }
+};
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Where a decode unit stages wave w's K and V tiles (and, at the end, its
+// fp32 output rows in the K tile).  One contiguous array when the kernel runs
+// decode units only: the V tile is the K tile plus a constant, which keeps
+// the operand addresses in few registers.  The eight-slot pool when decode
+// and prefill units share a kernel.
+template <int TILEH>
+struct ContigDecodeLds {
+  uint16_t *base;
+  __device__ uint16_t *k(int w) const { return base + w * 2 * TILEH; }
+  __device__ uint16_t *v(int w) const { return k(w) + TILEH; }
+  __device__ uint16_t *k_const(int w) const { return k(w); }
+};
+struct PoolDecodeLds {
+  LdsPool pool;
+  __device__ uint16_t *k(int w) const { return pool.pick(2 * w); }
+  __device__ uint16_t *v(int w) const { return pool.pick(2 * w + 1); }
+  __device__ uint16_t *k_const(int w) const { return pool.s(2 * w); }
+};
+
+// s_waitcnt immediate (gfx9 fields): vmcnt (bits 3:0 and 15:14), expcnt 7 (no
+// wait, bits 6:4), lgkmcnt (bits 11:8).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+// All but the newest `VM` of this wave's loads (LDS-destination loads
+// included; loads complete in issue order) and all its LDS operations
+// complete, then a workgroup barrier: afterwards every wave sees whatever any
+// wave loaded into LDS before those VM, and no wave still reads a slot that is
+// about to be refilled.  The signal fences keep the compiler from moving
+// memory accesses across the barrier.
+template <int VM>
+__device__ inline void wait_then_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+}  // namespace pa
