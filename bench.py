@@ -70,7 +70,7 @@ def causal_flops(case):
 KERNEL_SOURCES = ("paged_kv_cache_lds_amd/csrc/pa_device.h", "paged_kv_cache_lds_amd/csrc/pa_common.h",
                   "paged_kv_cache_lds_amd/csrc/pa_decode.h", "paged_kv_cache_lds_amd/csrc/pa_kernels.h",
                   "paged_kv_cache_lds_amd/csrc/paged_attn.hip")
-TRAFFIC_PROFILE = "profiles/attn_fwd_mha_decode_b256_ctx4096.txt"
+TRAFFIC_PROFILE = "profiles/attn_decode_mha_decode_b256_ctx4096.txt"
 
 
 def measured_traffic(batch, ctx):
