@@ -9,15 +9,15 @@ namespace pa {
 
 
 // Work decomposition constants.
-constexpr int kThreads = 256;     // four wave64 per workgroup
+constexpr int kThreads = 256;     // append and combine kernels: four wave64
 constexpr int kWaves = 4;
+constexpr int kUThreads = 512;    // attention kernels: eight wave64, two per SIMD
+constexpr int kUWaves = 8;
 constexpr int kKeyTile = 32;      // decode: keys per wave main-loop iteration
 constexpr int kDecodeRows = 16;   // packed (token, q-head) rows of a decode unit
-constexpr int kPrefillRB = 1;     // 32-row MFMA blocks per wave in a prefill unit
-constexpr int kPrefillRows = 32 * kPrefillRB * kWaves;   // rows of a prefill unit
+constexpr int kPrefillRows = 32 * kUWaves;   // rows of a prefill unit (32 per wave)
 constexpr int kPTile = 32;        // prefill: keys per workgroup main-loop iteration
 constexpr int kMaxSplits = 128;
-constexpr int kWindow = 64;       // block-table entries a wave holds at once (one per lane)
 
 struct FwdParams {
   const uint16_t *q;
@@ -115,6 +115,7 @@ __device__ inline int decode_tiles(int K_b) { return (K_b + kKeyTile - 1) / kKey
 
 // inclusive prefix sum over the workgroup (every thread contributes x);
 // `total` receives the workgroup sum
+template <int NW>
 __device__ inline int block_inclusive_scan(int x, int *s_wsum, int &total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
@@ -127,7 +128,7 @@ __device__ inline int block_inclusive_scan(int x, int *s_wsum, int &total) {
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int v = s_wsum[w];
     before += (w < wave) ? v : 0;
     total += v;
@@ -146,6 +147,7 @@ struct UnitInfo {
   int b, off, splits;   // off = split (decode) or query tile (prefill)
 };
 
+template <int NT>
 __device__ inline bool locate_unit(const FwdParams &p, int unit, UnitInfo &u, int *s_wsum,
                                    int *s_found) {
   const int tid = threadIdx.x;
@@ -154,7 +156,7 @@ __device__ inline bool locate_unit(const FwdParams &p, int unit, UnitInfo &u, in
   long extra = 0, total_tiles = 0;
   if (S > 1) {
     long n_dec = 0, tiles = 0;
-    for (int c0 = 0; c0 < p.batch; c0 += kThreads) {
+    for (int c0 = 0; c0 < p.batch; c0 += NT) {
       const int bb = c0 + tid;
       int dec = 0, t = 0;
       if (bb < p.batch) {
@@ -166,8 +168,8 @@ __device__ inline bool locate_unit(const FwdParams &p, int unit, UnitInfo &u, in
         }
       }
       int tot_d, tot_t;
-      block_inclusive_scan(dec, s_wsum, tot_d);
-      block_inclusive_scan(t, s_wsum, tot_t);
+      block_inclusive_scan<NT / 64>(dec, s_wsum, tot_d);
+      block_inclusive_scan<NT / 64>(t, s_wsum, tot_t);
       n_dec += tot_d;
       tiles += tot_t;
     }
@@ -178,7 +180,7 @@ __device__ inline bool locate_unit(const FwdParams &p, int unit, UnitInfo &u, in
   if (tid == 0) s_found[0] = -1;
   __syncthreads();
   int carry = 0;
-  for (int c0 = 0; c0 < p.batch; c0 += kThreads) {
+  for (int c0 = 0; c0 < p.batch; c0 += NT) {
     const int bb = c0 + tid;
     int units = 0, splits = 1;
     if (bb < p.batch) {
@@ -194,7 +196,7 @@ __device__ inline bool locate_unit(const FwdParams &p, int unit, UnitInfo &u, in
       }
     }
     int total;
-    const int incl = carry + block_inclusive_scan(units, s_wsum, total);
+    const int incl = carry + block_inclusive_scan<NT / 64>(units, s_wsum, total);
     const int excl = incl - units;
     if (units > 0 && unit >= excl && unit < incl) {
       s_found[0] = bb;
@@ -260,30 +262,31 @@ __device__ inline u32x2 lds_read_tr16(const uint16_t *p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// The eight LDS slots of a workgroup, one 32-row [key][D] tile each.  They
-// are separate LDS objects so that the compiler can tell a slot being filled
-// by LDS-destination loads from one being read, and keep those loads in
-// flight across the reads.
-constexpr int kSlots = 8;
+// The LDS slots of a workgroup, one 32-row [key][D] tile each (sixteen in the
+// unified kernel).  They are separate LDS objects so that the compiler can
+// tell a slot being filled by LDS-destination loads from one being read, and
+// keep those loads in flight across the reads.
+constexpr int kSlots = 16;
 struct LdsPool {
-  uint16_t *s0, *s1, *s2, *s3, *s4, *s5, *s6, *s7;
+  uint16_t *sl[kSlots];
   // slot i for a constant i
-  __device__ uint16_t *s(int i) const {
-    return i < 4 ? (i < 2 ? (i == 0 ? s0 : s1) : (i == 2 ? s2 : s3))
-                 : (i < 6 ? (i == 4 ? s4 : s5) : (i == 6 ? s6 : s7));
-  }
+  __device__ uint16_t *s(int i) const { return sl[i]; }
   // slot i for a run-time i.  The empty asm makes the candidates opaque, so
   // the selection stays a few scalar selects instead of becoming a table of
-  // LDS addresses (which a static initializer cannot hold).
+  // LDS addresses (which a static initializer cannot hold); the pointers stay
+  // in the LDS address space, so accesses through the result are LDS accesses.
   __device__ uint16_t *pick(int i) const {
     typedef __attribute__((address_space(3))) uint16_t lds_u16;
-    lds_u16 *a0 = (lds_u16 *)s0, *a1 = (lds_u16 *)s1, *a2 = (lds_u16 *)s2, *a3 = (lds_u16 *)s3;
-    lds_u16 *a4 = (lds_u16 *)s4, *a5 = (lds_u16 *)s5, *a6 = (lds_u16 *)s6, *a7 = (lds_u16 *)s7;
-    asm volatile("" : "+s"(a0), "+s"(a1), "+s"(a2), "+s"(a3), "+s"(a4), "+s"(a5), "+s"(a6),
-                      "+s"(a7));
-    lds_u16 *r = i < 4 ? (i < 2 ? (i == 0 ? a0 : a1) : (i == 2 ? a2 : a3))
-                       : (i < 6 ? (i == 4 ? a4 : a5) : (i == 6 ? a6 : a7));
-    return (uint16_t *)r;   // still known to be LDS to the address-space inference
+    lds_u16 *a[kSlots];
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k) {
+      a[k] = (lds_u16 *)sl[k];
+      asm volatile("" : "+s"(a[k]));
+    }
+    lds_u16 *r = a[0];
+#pragma unroll
+    for (int k = 1; k < kSlots; ++k) r = i == k ? a[k] : r;
+    return (uint16_t *)r;
   }
 };
 typedef __attribute__((address_space(3))) void lds_void;

@@ -7,30 +7,29 @@ namespace pa {
 
 // ---------------------------------------------------------------------------
 // Decode unit: <= 16 packed rows (the G q heads of one kv head for one or a
-// few tokens), one split of the sequence's keys.  The four waves share the
-// rows and each walks a contiguous quarter of the split's 32-key tiles:
+// few tokens), one split of the sequence's keys.  The waves (four, or eight in
+// the unified kernel) share the rows and each walks a contiguous share of the
+// split's 32-key tiles:
 //
-//   page window  each lane holds the physical id of one of the next 64
-//                logical pages (one table load per 64 pages); the one or two
-//                pages a tile touches are read out of the window with scalar
-//                lane reads, so no table access sits between tiles; ids are
-//                resolved by absolute logical index, and entries past the
-//                last visible page are never read;
+//   page ids     a tile's one or two page ids are fetched four tiles ahead
+//                with one vector load (lane i holds the page of load
+//                instruction i) and moved to scalar registers with lane
+//                reads; ids are resolved by absolute logical index, and
+//                entries past the last visible page are never read;
 //   row loads    every load instruction fetches whole K (V) rows: D*2 bytes
 //                per key, 64*16/(D*2) keys per instruction, which streams
 //                HBM faster than MFMA-shaped partial-row loads; two tiles are
 //                in flight per wave (tile t + 2 is issued as soon as tile t's
 //                registers are staged);
-//   LDS staging  K and V land in the wave's own LDS region, rows with their
-//                16-byte chunks XOR-swizzled by key, so both the MFMA-layout
-//                K reads and the transposing V reads are bank-conflict free;
-//                no workgroup barrier in the loop;
+//   LDS staging  K and V land in the wave's own LDS slots, rows with their
+//                16-byte chunks XOR-swizzled by key; no workgroup barrier in
+//                the loop;
 //   S^T = K Q^T  16x16x32 MFMA, keys on M: each lane's probabilities are
 //                already the B operand of the PV product;
 //   O^T += V^T P^T 16x16x32 MFMA on key-contiguous V^T from transposing reads.
 // The waves' (max, sum, O) states merge through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int DT, int D, class Lds>
+template <int DT, int D, int NW, class Lds>
 __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, const int g,
                                             const int split, const int S_b, const SeqInfo si,
                                             const Lds &lds, float (*sm_m)[kDecodeRows],
@@ -58,8 +57,8 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
   const int t_end = (int)((long)(split + 1) * n_t / S_b);
   const int key_end = min(t_end * kKeyTile, bound);
   const int n_w = t_end - t_begin;
-  const int w_begin = t_begin + wave * (n_w >> 2) + min(wave, n_w & 3);
-  const int w_end = w_begin + (n_w >> 2) + (wave < (n_w & 3) ? 1 : 0);
+  const int w_begin = t_begin + wave * (n_w / NW) + min(wave, n_w % NW);
+  const int w_end = w_begin + n_w / NW + (wave < n_w % NW ? 1 : 0);
   // keys of this wave: [w_begin * 32, key_end_w); tiles past w_end (the
   // pipeline's tail) read nothing and are fully masked
   const int key_end_w = min(w_end * kKeyTile, key_end);
@@ -273,14 +272,14 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
   if (orow >= rows_b) return;
   float M = kNegInf;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][orow]);
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][orow]);
   float acc[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) acc[c] = 0.f;
   float L = 0.f;
   if (M != kNegInf) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float wt = fast_exp2(sm_m[w][orow] - M);   // 0 for waves that saw nothing
       L += wt * sm_l[w][orow];
       const float *src = reinterpret_cast<const float *>(lds.k_const(w)) + orow * D + oc * CH;

@@ -16,25 +16,13 @@ namespace pa {
 
 template <int DT, int D, bool kUnified>
 __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
-  // decode-only kernel: one contiguous array, a K and a V tile per wave;
-  // unified kernel: eight separate 32-row slots (four K and four V slots of a
-  // prefill unit; a K/V pair per wave of a decode unit)
-  // (K slots of a prefill unit at D = 128 carry 64 halves of padding per two
-  // 1 KiB blocks)
-  constexpr int kSlotH = kKeyTile * D + (D == 128 ? 4 * 64 : 0);
-  static_assert(kPTile == kKeyTile, "prefill and decode tiles share the slots");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_s0[kUnified ? kSlotH : kSlots * kKeyTile * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_s1[kUnified ? kSlotH : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_s2[kUnified ? kSlotH : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_s3[kUnified ? kSlotH : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_s4[kUnified ? kSlotH : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_s5[kUnified ? kSlotH : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_s6[kUnified ? kSlotH : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_s7[kUnified ? kSlotH : 8];
-  const LdsPool pool{lds_s0, lds_s1, lds_s2, lds_s3, lds_s4, lds_s5, lds_s6, lds_s7};
-  __shared__ float sm_m[kWaves][kDecodeRows];
-  __shared__ float sm_l[kWaves][kDecodeRows];
-  __shared__ int s_wsum[kWaves];
+  // both kernels run eight waves and split a decode unit's keys the same
+  // way, so a sequence's result does not depend on which kernel - or which
+  // batch - it ran in
+  constexpr int NW = kUWaves;
+  __shared__ float sm_m[NW][kDecodeRows];
+  __shared__ float sm_l[NW][kDecodeRows];
+  __shared__ int s_wsum[NW];
   __shared__ int s_found[3];
 
   const int g = blockIdx.x % p.hkv;
@@ -45,7 +33,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     u.off = 0;
     u.splits = 1;
     if (u.b >= p.batch) return;
-  } else if (!locate_unit(p, unit, u, s_wsum, s_found)) {
+  } else if (!locate_unit<NW * 64>(p, unit, u, s_wsum, s_found)) {
     return;
   }
   // the unit and its sequence are the same for every lane: keep them in SGPRs
@@ -59,35 +47,78 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   si.K_b = __builtin_amdgcn_readfirstlane(si.K_b);
   const int rows_b = si.q_len * p.group;
   if (rows_b <= 0) return;
-  if (!kUnified || p.all_decode || rows_b <= kDecodeRows) {
-    if (g == 0 && u.off == 0 && p.split_count != nullptr && threadIdx.x == 0)
-      p.split_count[u.b] = u.splits;
-    if constexpr (kUnified)
-      decode_unit<DT, D>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds{pool}, sm_m, sm_l);
-    else
-      decode_unit<DT, D>(p, u.b, g, u.off, u.splits, si, ContigDecodeLds<kKeyTile * D>{lds_s0}, sm_m,
-                         sm_l);
-  } else if constexpr (kUnified) {
-    const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
-    if (p.geom.table != nullptr)
-      prefill_unit<DT, D, true>(p, u.b, g, n_qt - 1 - u.off, si, pool);
-    else
-      prefill_unit<DT, D, false>(p, u.b, g, n_qt - 1 - u.off, si, pool);
+  const bool decode = !kUnified || p.all_decode || rows_b <= kDecodeRows;
+  if (decode && g == 0 && u.off == 0 && p.split_count != nullptr && threadIdx.x == 0)
+    p.split_count[u.b] = u.splits;
+
+  if constexpr (!kUnified) {
+    // decode-only kernel: one contiguous array, a K and a V tile per wave
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kUWaves * 2 * kKeyTile * D];
+    decode_unit<DT, D, kUWaves>(p, u.b, g, u.off, u.splits, si, ContigDecodeLds<kKeyTile * D>{lds},
+                                sm_m, sm_l);
+  } else {
+    // unified kernel: sixteen separate 32-row slots - a K/V pair per wave of a
+    // decode unit, four K and four V slots of a prefill unit (K slots at
+    // D = 128 carry 64 halves of padding per two 1 KiB blocks)
+    constexpr int kSlotH = kKeyTile * D + (D == 128 ? 3 * 64 : 0);
+    static_assert(kPTile == kKeyTile, "prefill and decode tiles share the slots");
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s0[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s1[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s2[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s3[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s4[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s5[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s6[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s7[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s8[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s9[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s10[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s11[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s12[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s13[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s14[kSlotH];
+    __shared__ __attribute__((aligned(256))) uint16_t lds_s15[kSlotH];
+    LdsPool pool;
+    pool.sl[0] = lds_s0;
+    pool.sl[1] = lds_s1;
+    pool.sl[2] = lds_s2;
+    pool.sl[3] = lds_s3;
+    pool.sl[4] = lds_s4;
+    pool.sl[5] = lds_s5;
+    pool.sl[6] = lds_s6;
+    pool.sl[7] = lds_s7;
+    pool.sl[8] = lds_s8;
+    pool.sl[9] = lds_s9;
+    pool.sl[10] = lds_s10;
+    pool.sl[11] = lds_s11;
+    pool.sl[12] = lds_s12;
+    pool.sl[13] = lds_s13;
+    pool.sl[14] = lds_s14;
+    pool.sl[15] = lds_s15;
+    if (decode) {
+      decode_unit<DT, D, kUWaves>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds{pool}, sm_m, sm_l);
+    } else {
+      const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
+      if (p.geom.table != nullptr)
+        prefill_unit<DT, D, true>(p, u.b, g, n_qt - 1 - u.off, si, pool);
+      else
+        prefill_unit<DT, D, false>(p, u.b, g, n_qt - 1 - u.off, si, pool);
+    }
   }
 }
 
 // Decode-only batches (every sequence fits a decode unit, known on the host):
-// two waves per SIMD.
+// eight waves, two per SIMD.
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kUThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_decode_kernel(FwdParams p) {
   attn_fwd_body<DT, D, false>(p);
 }
 
-// Unified kernel for any mix of prefill and decode sequences: two waves per
-// SIMD as well.
+// Unified kernel for any mix of prefill and decode sequences: eight waves,
+// two per SIMD, one workgroup per CU.
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kUThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
   attn_fwd_body<DT, D, true>(p);
 }

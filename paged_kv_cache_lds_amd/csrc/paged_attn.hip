@@ -188,10 +188,10 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   p.all_decode = pl.all_decode;
   if (pl.grid > 0x7fffffffL) return PA_ERR_SHAPE;
   if (pl.all_decode)
-    hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(kThreads),
+    hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(pa::kUThreads),
                        0, stream, p);
   else
-    hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(pa::kUThreads), 0,
                        stream, p);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (pl.splits > 1) {
