@@ -9,9 +9,9 @@ namespace pa {
 
 
 // Work decomposition constants.
-constexpr int kThreads = 256;     // append and combine kernels: four wave64
+constexpr int kThreads = 256;     // decode-only kernel (and append, combine): four wave64
 constexpr int kWaves = 4;
-constexpr int kUThreads = 512;    // attention kernels: eight wave64, two per SIMD
+constexpr int kUThreads = 512;    // unified kernel: eight wave64, two per SIMD
 constexpr int kUWaves = 8;
 constexpr int kKeyTile = 32;      // decode: keys per wave main-loop iteration
 constexpr int kDecodeRows = 16;   // packed (token, q-head) rows of a decode unit
@@ -137,49 +137,65 @@ __device__ inline int block_inclusive_scan(int x, int *s_wsum, int &total) {
   return before + x;
 }
 
-// Unified work mapping.  Units per kv head: a sequence whose packed rows
-// (q_len * group) fit one 16-row decode unit gets seq_splits() units (its
-// keys split across workgroups); a longer one gets cdiv(rows, 128) prefill
-// units, heaviest (last, under the causal mask) first.  The host sizes the
-// grid from static maxima; each workgroup finds its (sequence, unit) by
-// block-wide scans over the device metadata, and surplus workgroups return.
+// Work mapping.  Units per kv head, prefill units first: a sequence whose
+// packed rows (q_len * group) exceed one 16-row decode unit gets
+// cdiv(rows, kPrefillRows) prefill units, heaviest (last, under the causal
+// mask) first; then every other sequence gets seq_splits() decode units (its
+// keys split across units).  A workgroup of the decode-only kernel takes one
+// decode unit; one of the unified kernel takes one prefill unit or two
+// consecutive decode units, one per four-wave half, so that a decode unit
+// runs the same four-wave code in either kernel.  The host sizes the grid
+// from static maxima; every workgroup finds its units by block-wide scans
+// over the device metadata, and a workgroup or half without a unit returns.
 struct UnitInfo {
   int b, off, splits;   // off = split (decode) or query tile (prefill)
 };
 
-template <int NT>
-__device__ inline bool locate_unit(const FwdParams &p, int unit, UnitInfo &u, int *s_wsum,
-                                   int *s_found) {
+template <int NT, int kDecPerWg>
+__device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool &decode,
+                                   int *s_wsum, int *s_found) {
   const int tid = threadIdx.x;
+  const int half = kDecPerWg == 2 ? tid / (NT / 2) : 0;
   const int S = p.num_splits;
-  // pass 1: decode-mode sequence count and their key tiles
-  long extra = 0, total_tiles = 0;
-  if (S > 1) {
+  auto is_decode = [&](int rows) { return p.all_decode || rows <= kDecodeRows; };
+  // pass 1: prefill units, and (split budget) decode-mode sequences and their key tiles
+  long extra = 0, total_tiles = 0, n_pre = 0;
+  if (S > 1 || !p.all_decode) {
     long n_dec = 0, tiles = 0;
     for (int c0 = 0; c0 < p.batch; c0 += NT) {
       const int bb = c0 + tid;
-      int dec = 0, t = 0;
+      int dec = 0, t = 0, pre = 0;
       if (bb < p.batch) {
         const SeqInfo si = seq_info(p, bb);
         const int rows = si.q_len * p.group;
-        if (rows > 0 && (p.all_decode || rows <= kDecodeRows)) {
-          dec = 1;
-          t = decode_tiles(si.K_b);
+        if (rows > 0) {
+          if (is_decode(rows)) {
+            dec = 1;
+            t = decode_tiles(si.K_b);
+          } else {
+            pre = (rows + kPrefillRows - 1) / kPrefillRows;
+          }
         }
       }
-      int tot_d, tot_t;
-      block_inclusive_scan<NT / 64>(dec, s_wsum, tot_d);
-      block_inclusive_scan<NT / 64>(t, s_wsum, tot_t);
+      int tot_d = 0, tot_t = 0, tot_p = 0;
+      if (S > 1) {
+        block_inclusive_scan<NT / 64>(dec, s_wsum, tot_d);
+        block_inclusive_scan<NT / 64>(t, s_wsum, tot_t);
+      }
+      if (!p.all_decode) block_inclusive_scan<NT / 64>(pre, s_wsum, tot_p);
       n_dec += tot_d;
       tiles += tot_t;
+      n_pre += tot_p;
     }
     extra = n_dec * (S - 1);
     total_tiles = tiles;
   }
-  // pass 2: prefix of units, find ours
-  if (tid == 0) s_found[0] = -1;
+  // pass 2: prefix over the units of our kind, find ours (one per half)
+  const bool pre_wg = wg < n_pre;
+  const long first = pre_wg ? wg : (wg - n_pre) * kDecPerWg;   // first unit index sought
+  if (tid < 6) s_found[tid] = -1;
   __syncthreads();
-  int carry = 0;
+  long carry = 0;
   for (int c0 = 0; c0 < p.batch; c0 += NT) {
     const int bb = c0 + tid;
     int units = 0, splits = 1;
@@ -187,29 +203,35 @@ __device__ inline bool locate_unit(const FwdParams &p, int unit, UnitInfo &u, in
       const SeqInfo si = seq_info(p, bb);
       const int rows = si.q_len * p.group;
       if (rows > 0) {
-        if (p.all_decode || rows <= kDecodeRows) {
+        if (is_decode(rows)) {
           splits = seq_splits(extra, decode_tiles(si.K_b), total_tiles);
-          units = splits;
-        } else {
+          if (!pre_wg) units = splits;
+        } else if (pre_wg) {
           units = (rows + kPrefillRows - 1) / kPrefillRows;
         }
       }
     }
     int total;
-    const int incl = carry + block_inclusive_scan<NT / 64>(units, s_wsum, total);
-    const int excl = incl - units;
-    if (units > 0 && unit >= excl && unit < incl) {
-      s_found[0] = bb;
-      s_found[1] = unit - excl;
-      s_found[2] = splits;
+    const long incl = carry + block_inclusive_scan<NT / 64>(units, s_wsum, total);
+    const long excl = incl - units;
+    const int n_sought = pre_wg ? 1 : kDecPerWg;
+    for (int h = 0; h < n_sought; ++h) {
+      const long want = first + h;
+      if (units > 0 && want >= excl && want < incl) {
+        s_found[3 * h] = bb;
+        s_found[3 * h + 1] = (int)(want - excl);
+        s_found[3 * h + 2] = splits;
+      }
     }
     carry += total;
     __syncthreads();
-    if (s_found[0] >= 0) break;
+    if (s_found[3 * (n_sought - 1)] >= 0) break;   // the last one sought is found
   }
-  u.b = s_found[0];
-  u.off = s_found[1];
-  u.splits = s_found[2];
+  const int slot = pre_wg ? 0 : 3 * half;
+  u.b = s_found[slot];
+  u.off = s_found[slot + 1];
+  u.splits = s_found[slot + 2];
+  decode = !pre_wg;
   return u.b >= 0;
 }
 
@@ -303,11 +325,12 @@ struct ContigDecodeLds {
   __device__ uint16_t *v(int w) const { return k(w) + TILEH; }
   __device__ uint16_t *k_const(int w) const { return k(w); }
 };
+template <int H>   // a four-wave half of the unified kernel: slots 8 H .. 8 H + 7
 struct PoolDecodeLds {
   LdsPool pool;
-  __device__ uint16_t *k(int w) const { return pool.pick(2 * w); }
-  __device__ uint16_t *v(int w) const { return pool.pick(2 * w + 1); }
-  __device__ uint16_t *k_const(int w) const { return pool.s(2 * w); }
+  __device__ uint16_t *k(int w) const { return pool.pick(2 * w + 8 * H); }
+  __device__ uint16_t *v(int w) const { return pool.pick(2 * w + 1 + 8 * H); }
+  __device__ uint16_t *k_const(int w) const { return pool.s(2 * w + 8 * H); }
 };
 
 // s_waitcnt immediate (gfx9 fields): vmcnt (bits 3:0 and 15:14), expcnt 7 (no

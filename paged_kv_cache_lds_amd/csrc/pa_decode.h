@@ -7,9 +7,10 @@ namespace pa {
 
 // ---------------------------------------------------------------------------
 // Decode unit: <= 16 packed rows (the G q heads of one kv head for one or a
-// few tokens), one split of the sequence's keys.  The waves (four, or eight in
-// the unified kernel) share the rows and each walks a contiguous share of the
-// split's 32-key tiles:
+// few tokens), one split of the sequence's keys, on four waves (a workgroup of
+// the decode-only kernel, or one half of a unified-kernel workgroup).  The
+// waves share the rows and each walks a contiguous share of the split's 32-key
+// tiles:
 //
 //   page ids     a tile's one or two page ids are fetched four tiles ahead
 //                with one vector load (lane i holds the page of load
@@ -27,7 +28,8 @@ namespace pa {
 //   S^T = K Q^T  16x16x32 MFMA, keys on M: each lane's probabilities are
 //                already the B operand of the PV product;
 //   O^T += V^T P^T 16x16x32 MFMA on key-contiguous V^T from transposing reads.
-// The waves' (max, sum, O) states merge through LDS at the end.
+// The waves' (max, sum, O) states merge through LDS at the end, after the
+// unit's only workgroup barrier (a half without a unit meets it on its own).
 // ---------------------------------------------------------------------------
 template <int DT, int D, int NW, class Lds>
 __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, const int g,
@@ -42,7 +44,7 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
   constexpr int ROWH = D;          // halves per staged row (no padding: swizzled)
   constexpr int TILEH = kKeyTile * ROWH;          // halves per staged tile (one LDS slot)
   static_assert(TILEH * 2 >= kDecodeRows * D * 4, "a K slot must hold the wave's O staging");
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x & (NW * 64 - 1);   // within the unit's waves
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int lr = lane & 15;

@@ -16,28 +16,37 @@ namespace pa {
 
 template <int DT, int D, bool kUnified>
 __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
-  // both kernels run eight waves and split a decode unit's keys the same
-  // way, so a sequence's result does not depend on which kernel - or which
-  // batch - it ran in
-  constexpr int NW = kUWaves;
-  __shared__ float sm_m[NW][kDecodeRows];
-  __shared__ float sm_l[NW][kDecodeRows];
+  constexpr int NW = kUnified ? kUWaves : kWaves;   // waves of the workgroup
+  __shared__ float sm_m[NW][kDecodeRows];           // per-wave decode states (two halves
+  __shared__ float sm_l[NW][kDecodeRows];           // of four in the unified kernel)
   __shared__ int s_wsum[NW];
-  __shared__ int s_found[3];
+  __shared__ int s_found[6];
 
   const int g = blockIdx.x % p.hkv;
-  const int unit = blockIdx.x / p.hkv;
+  const int wg = blockIdx.x / p.hkv;
   UnitInfo u;
-  if (p.all_decode && p.num_splits == 1) {
-    u.b = unit;
+  bool decode = true;
+  bool have = true;
+  if (!kUnified && p.num_splits == 1) {   // decode-only, one unit per sequence
+    u.b = wg;
     u.off = 0;
     u.splits = 1;
-    if (u.b >= p.batch) return;
-  } else if (!locate_unit<NW * 64>(p, unit, u, s_wsum, s_found)) {
+    have = u.b < p.batch;
+  } else {
+    have = locate_unit<NW * 64, kUnified ? 2 : 1>(p, wg, u, decode, s_wsum, s_found);
+  }
+  // A half of the unified kernel without a decode unit still meets the one
+  // workgroup barrier of the other half's decode unit.
+  auto idle_half = [&]() {
+    if (kUnified && decode) __syncthreads();
+  };
+  if (!have) {
+    idle_half();
     return;
   }
-  // the unit and its sequence are the same for every lane: keep them in SGPRs
-  // (page indices, buffer descriptors and uniform offsets derive from them)
+  // the unit and its sequence are the same for every lane of a wave: keep
+  // them in SGPRs (page indices, buffer descriptors and uniform offsets derive
+  // from them)
   u.b = __builtin_amdgcn_readfirstlane(u.b);
   u.off = __builtin_amdgcn_readfirstlane(u.off);
   u.splits = __builtin_amdgcn_readfirstlane(u.splits);
@@ -46,16 +55,19 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   si.q_len = __builtin_amdgcn_readfirstlane(si.q_len);
   si.K_b = __builtin_amdgcn_readfirstlane(si.K_b);
   const int rows_b = si.q_len * p.group;
-  if (rows_b <= 0) return;
-  const bool decode = !kUnified || p.all_decode || rows_b <= kDecodeRows;
-  if (decode && g == 0 && u.off == 0 && p.split_count != nullptr && threadIdx.x == 0)
+  if (rows_b <= 0) {   // only in the single-split decode-only mapping
+    idle_half();
+    return;
+  }
+  if (decode && g == 0 && u.off == 0 && p.split_count != nullptr &&
+      (threadIdx.x & (kWaves * 64 - 1)) == 0)
     p.split_count[u.b] = u.splits;
 
   if constexpr (!kUnified) {
     // decode-only kernel: one contiguous array, a K and a V tile per wave
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[kUWaves * 2 * kKeyTile * D];
-    decode_unit<DT, D, kUWaves>(p, u.b, g, u.off, u.splits, si, ContigDecodeLds<kKeyTile * D>{lds},
-                                sm_m, sm_l);
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kWaves * 2 * kKeyTile * D];
+    decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si, ContigDecodeLds<kKeyTile * D>{lds},
+                               sm_m, sm_l);
   } else {
     // unified kernel: sixteen separate 32-row slots - a K/V pair per wave of a
     // decode unit, four K and four V slots of a prefill unit (K slots at
@@ -96,7 +108,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     pool.sl[14] = lds_s14;
     pool.sl[15] = lds_s15;
     if (decode) {
-      decode_unit<DT, D, kUWaves>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds{pool}, sm_m, sm_l);
+      if (threadIdx.x < kWaves * 64)
+        decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds<0>{pool}, sm_m,
+                                   sm_l);
+      else
+        decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds<1>{pool},
+                                   sm_m + kWaves, sm_l + kWaves);
     } else {
       const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
       if (p.geom.table != nullptr)
@@ -108,9 +125,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
 }
 
 // Decode-only batches (every sequence fits a decode unit, known on the host):
-// eight waves, two per SIMD.
+// four waves, two workgroups per CU.
 template <int DT, int D>
-__global__ __launch_bounds__(kUThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_decode_kernel(FwdParams p) {
   attn_fwd_body<DT, D, false>(p);
 }

@@ -108,8 +108,15 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
                   ? a->num_splits
                   : paged_attn_num_splits(a->batch, a->total_q, a->num_heads_q, a->num_heads_kv,
                                           a->head_dim, a->max_seqlen_q, pl.max_seqlen_k, num_cus);
+  // workgroups per kv head: one per decode unit (decode-only kernel); one per
+  // prefill unit plus one per two decode units (unified kernel).  Decode
+  // units number at most batch * splits; prefill units, sum over sequences of
+  // cdiv(rows_b, kPrefillRows), at most cdiv(total rows, kPrefillRows) +
+  // batch - 1.
   long units_per_head = (long)a->batch * pl.splits;
-  if (!pl.all_decode) units_per_head += cdiv((long)a->total_q * group, pa::kPrefillRows);
+  if (!pl.all_decode)
+    units_per_head = cdiv(units_per_head, 2) + cdiv((long)a->total_q * group, pa::kPrefillRows) +
+                     a->batch - 1;
   pl.grid = units_per_head * a->num_heads_kv;
   if (pl.splits > 1) {
     // the device shares the budget by sequence length (one split each, the
@@ -188,7 +195,7 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   p.all_decode = pl.all_decode;
   if (pl.grid > 0x7fffffffL) return PA_ERR_SHAPE;
   if (pl.all_decode)
-    hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(pa::kUThreads),
+    hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(kThreads),
                        0, stream, p);
   else
     hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(pa::kUThreads), 0,
