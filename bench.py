@@ -150,7 +150,7 @@ def sweep(name, reps, out_path):
         fh.flush()
         print(json.dumps(rec), file=sys.stderr, flush=True)
 
-    def run(case, inp, num_splits=None, max_seqlen_k=None, seqlens=None, append=None):
+    def make_call(case, inp, num_splits=None, max_seqlen_k=None, seqlens=None, append=None):
         kn = inp.k_new if (append if append is not None else case.append) else None
         vn = inp.v_new if kn is not None else None
         seq = inp.cache_seqlens if seqlens is None else seqlens
@@ -171,6 +171,10 @@ def sweep(name, reps, out_path):
                               max_seqlen_k=args.max_seqlen_k, k_new=kn, v_new=vn,
                               causal=case.causal, num_splits=args.num_splits, out=out,
                               softmax_lse=lse, workspace=ws)
+        return S, call
+
+    def run(case, inp, **kw):
+        S, call = make_call(case, inp, **kw)
         call()
         torch.cuda.synchronize()
         med, mn = median_call_ms(call, reps, torch, flush)
@@ -258,6 +262,38 @@ def sweep(name, reps, out_path):
                       "two_call_ms": dmed + pmed})
                 del inp, di, pi
                 torch.cuda.empty_cache()
+    elif name == "graph":
+        # the same call eager and replayed from a HIP graph (launch overhead of
+        # small, latency-bound calls); the buffers stay fixed, so one capture
+        # replays the identical work
+        points = (("mha_decode_b1_ctx512", wl.mha_decode(1, 512)),
+                  ("mha_decode_b8_ctx1024", wl.mha_decode(8, 1024)),
+                  ("unified_varlen_nq100_h12x64", wl.unified_varlen(100, heads=12, head_dim=64)))
+        for label, c in points:
+            inp = wl.make_inputs(c, "cuda")
+            S, call = make_call(c, inp)
+            call()
+            torch.cuda.synchronize()
+            e_med, e_min = median_call_ms(call, reps, torch, flush)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                call()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call()
+            torch.cuda.synchronize()
+            g_med, g_min = median_call_ms(g.replay, reps, torch, flush)
+            # back to back: 200 calls queued from Python, no flush - the
+            # per-call rate when the host's launch cost is what limits
+            loop = lambda fn: time_calls(fn, 200, 10, torch)
+            emit({"sweep": "graph", "workload": label, "splits": S, "eager_ms": e_med,
+                  "eager_ms_min": e_min, "graph_ms": g_med, "graph_ms_min": g_min,
+                  "eager_loop_ms": loop(call), "graph_loop_ms": loop(g.replay)})
+            del g, inp
+            torch.cuda.empty_cache()
     fh.close()
 
 
@@ -272,7 +308,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
-    ap.add_argument("--sweep", choices=["copy", "decode", "gqa", "prefill", "unified"],
+    ap.add_argument("--sweep", choices=["copy", "decode", "gqa", "prefill", "unified", "graph"],
                     help="run a measurement sweep instead of the headline line")
     ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
     ap.add_argument("--reps", type=int, default=10)
