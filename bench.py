@@ -262,6 +262,22 @@ def sweep(name, reps, out_path):
                       "two_call_ms": dmed + pmed})
                 del inp, di, pi
                 torch.cuda.empty_cache()
+    elif name == "multitoken":
+        # decode with q_len new tokens per sequence (speculative scoring): one
+        # decode unit per sequence while q_len * G <= 16; HBM rate vs q_len = 1
+        for hq, hkv, B, ctx, qls in ((32, 32, 64, 2048, (1, 2, 4, 8, 16)),
+                                     (64, 8, 8, 16384, (1, 2))):
+            for ql in qls:
+                c = wl.multi_token_decode(B, ctx, ql, heads_q=hq, heads_kv=hkv,
+                                          dtype="f16" if hq == hkv else "bf16")
+                inp = wl.make_inputs(c, "cuda")
+                S, med, mn = run(c, inp)
+                by = algorithmic_bytes(c)
+                emit({"sweep": "multitoken", "heads": f"{hq}/{hkv}", "batch": B, "ctx": ctx,
+                      "q_len": ql, "splits": S, "ms": med, "ms_min": mn, "GBps": by / med / 1e6,
+                      "frac": by / med / 1e6 / HBM_PEAK_GBS})
+                del inp
+                torch.cuda.empty_cache()
     elif name == "graph":
         # the same call eager and replayed from a HIP graph (launch overhead of
         # small, latency-bound calls); the buffers stay fixed, so one capture
@@ -308,7 +324,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
-    ap.add_argument("--sweep", choices=["copy", "decode", "gqa", "prefill", "unified", "graph"],
+    ap.add_argument("--sweep", choices=["copy", "decode", "gqa", "prefill", "unified", "graph",
+                                        "multitoken"],
                     help="run a measurement sweep instead of the headline line")
     ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
     ap.add_argument("--reps", type=int, default=10)

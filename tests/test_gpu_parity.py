@@ -145,6 +145,16 @@ def test_unified_varlen(nq, heads, hd):
     run_parity(wl.unified_varlen(nq, heads=heads, head_dim=hd), splits=(None, 2))
 
 
+@pytest.mark.parametrize("q_len,hq,hkv,dtype", [(2, 32, 32, "f16"), (7, 32, 32, "f16"),
+                                                (16, 32, 32, "f16"), (2, 64, 8, "bf16")])
+def test_multi_token_decode(q_len, hq, hkv, dtype):
+    # q_len new tokens per sequence, q_len * G <= 16 packed rows: one decode unit
+    # per (sequence, split), causal over the appended tokens
+    c = wl.multi_token_decode(3, 700, q_len, heads_q=hq, heads_kv=hkv, dtype=dtype)
+    c.cache_seqlens = [700, 41, 1500]
+    run_parity(c, splits=(None, 3))
+
+
 def test_unified_varlen_with_prefix():
     run_parity(wl.unified_varlen(300, prefix=777))
 

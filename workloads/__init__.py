@@ -237,6 +237,16 @@ def causal_prefill_append(nq, prefix="zero", seed=3000) -> Case:
                 append=True, causal=True, seed=seed + nq)
 
 
+def multi_token_decode(batch, ctx, q_len, heads_q=32, heads_kv=32, dtype="f16", seed=5000) -> Case:
+    """speculative-decoding scoring: every sequence at cache `ctx` with `q_len`
+    new tokens (q_len * heads_q / heads_kv <= 16 packed rows, so one decode
+    unit each); head_dim 128, page 16, new K/V appended, causal."""
+    return Case(name=f"multi_token_decode_b{batch}_ctx{ctx}_q{q_len}_h{heads_q}x{heads_kv}",
+                q_lens=[q_len] * batch, cache_seqlens=[ctx] * batch, num_heads_q=heads_q,
+                num_heads_kv=heads_kv, head_dim=128, dtype=dtype, page_size=16, append=True,
+                causal=True, seed=seed + batch + ctx + q_len + heads_q)
+
+
 def unified_varlen(nq, heads=32, head_dim=128, prefix=0, seed=4000) -> Case:
     """one prefill chunk of nq tokens (cache `prefix`) plus 64 decode sequences of
     one token each with cache uniform in [512, 4096]; fp16, page 16, causal,
