@@ -16,7 +16,8 @@ two-key cases under ``tests/golden/``), invariance under physical page
 relabelling, page size and poisoned table tails, split-combine equals unsplit,
 causal decode equals non-causal, GQA equals MHA with repeated kv heads,
 varlen equals per-sequence calls, and bit-exact append against a numpy
-scatter.  No function here is "parity unpinned".
+scatter.  The rotary embedding (``rotary.py``) has pins of its own, listed in
+that module.  No function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -26,6 +27,8 @@ import os
 import subprocess
 
 import numpy as np
+
+from . import rotary as _rotary
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "paged_attn_oracle.c")
@@ -81,11 +84,13 @@ def bits_to_double(dtype: str, bits: int) -> float:
 
 
 def kv_append(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, k_new, v_new,
-              page_size=None, contig_alloc=0):
+              page_size=None, contig_alloc=0, rotary=None, dtype="f16"):
     """Return copies of the pools with the new rows written (bit copies).
 
     k_cache/v_cache: uint16 [num_pages, P, Hkv, D] (paged) or
-    [batch, alloc, Hkv, D] (contiguous, block_table None).
+    [batch, alloc, Hkv, D] (contiguous, block_table None).  With
+    ``rotary=(cos_bits, sin_bits, interleaved)`` the new keys are first rotated
+    at their positions cache_seqlens[b] + i (``oracle.rotary``); values never are.
     """
     kc = np.array(k_cache, dtype=np.uint16, copy=True, order="C")
     vc = np.array(v_cache, dtype=np.uint16, copy=True, order="C")
@@ -94,6 +99,11 @@ def kv_append(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, k_new,
     cu = _c(cu_seqlens_q, np.int32)
     kn = _c(k_new, np.uint16)
     vn = _c(v_new, np.uint16)
+    if rotary is not None:
+        cos_b, sin_b, inter = rotary
+        pos = _rotary.token_positions(seq, cu, appended=True, total=kn.shape[0])
+        kn = np.ascontiguousarray(_rotary.rotate_bits(kn, cos_b, sin_b, pos, dtype=dtype,
+                                                      interleaved=bool(inter)))
     batch = seq.shape[0]
     if bt is None:
         num_pages, P, hkv, d = kc.shape[0], kc.shape[1], kc.shape[2], kc.shape[3]
@@ -152,17 +162,25 @@ def attention(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *,
 
 def paged_attention(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q,
                     k_new=None, v_new=None, *, dtype="f16", causal=False, scale=None,
-                    threads=0):
-    """The whole call: append (if k_new/v_new), then attend.
+                    threads=0, rotary=None):
+    """The whole call: rotate (if ``rotary``), append (if k_new/v_new), then attend.
 
+    ``rotary=(cos_bits, sin_bits, interleaved)`` applies the rotary embedding of
+    ``oracle.rotary`` to the queries and the new keys, each token at its
+    position K_b - q_len_b + i, before anything else.
     Returns (out, lse, k_cache_after, v_cache_after).
     """
     if (k_new is None) != (v_new is None):
         raise ValueError("k_new and v_new go together")
+    if rotary is not None:
+        cos_b, sin_b, inter = rotary
+        pos = _rotary.token_positions(cache_seqlens, cu_seqlens_q, appended=k_new is not None,
+                                      total=np.asarray(q).shape[0])
+        q = _rotary.rotate_bits(q, cos_b, sin_b, pos, dtype=dtype, interleaved=bool(inter))
     kc, vc = k_cache, v_cache
     if k_new is not None:
         kc, vc = kv_append(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q,
-                           k_new, v_new)
+                           k_new, v_new, rotary=rotary, dtype=dtype)
     out, lse = attention(q, kc, vc, block_table, cache_seqlens, cu_seqlens_q, dtype=dtype,
                          appended=k_new is not None, causal=causal, scale=scale,
                          threads=threads)
