@@ -150,7 +150,8 @@ def sweep(name, reps, out_path):
         fh.flush()
         print(json.dumps(rec), file=sys.stderr, flush=True)
 
-    def make_call(case, inp, num_splits=None, max_seqlen_k=None, seqlens=None, append=None):
+    def make_call(case, inp, num_splits=None, max_seqlen_k=None, seqlens=None, append=None,
+                  rot=None):
         kn = inp.k_new if (append if append is not None else case.append) else None
         vn = inp.v_new if kn is not None else None
         seq = inp.cache_seqlens if seqlens is None else seqlens
@@ -164,13 +165,15 @@ def sweep(name, reps, out_path):
                             out=out, softmax_lse=lse)
         S = pa.paged_attn_splits_for(args)
         ws = torch.empty(max(1, pa.paged_attn_workspace_size(args)), dtype=torch.uint8, device="cuda")
+        rk = {} if rot is None else dict(rotary_cos=rot[0], rotary_sin=rot[1],
+                                         rotary_interleaved=rot[2])
 
         def call():
             pa.paged_attn_fwd(inp.q, inp.k_cache, inp.v_cache, inp.block_table, seq,
                               inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q,
                               max_seqlen_k=args.max_seqlen_k, k_new=kn, v_new=vn,
                               causal=case.causal, num_splits=args.num_splits, out=out,
-                              softmax_lse=lse, workspace=ws)
+                              softmax_lse=lse, workspace=ws, **rk)
         return S, call
 
     def run(case, inp, **kw):
@@ -278,6 +281,30 @@ def sweep(name, reps, out_path):
                       "frac": by / med / 1e6 / HBM_PEAK_GBS})
                 del inp
                 torch.cuda.empty_cache()
+    elif name == "rotary":
+        # the fused rotary embedding (q in the attention kernel, new keys in
+        # the append kernel) against the same call without it
+        points = (("mha_decode_b256_ctx4096_append", wl.mha_decode(256, 4096, append=True), 128),
+                  ("gqa_long_split_paged", wl.gqa_long_split(True), 128),
+                  ("causal_prefill_append_nq2048", wl.causal_prefill_append(2048, "zero"), 128),
+                  ("unified_varlen_nq500_h32x128", wl.unified_varlen(500), 128),
+                  ("unified_varlen_nq100_h12x64", wl.unified_varlen(100, heads=12, head_dim=64),
+                   64))
+        for label, c, rd in points:
+            inp = wl.make_inputs(c, "cuda")
+            cos, sin = wl.rotary_tables(max(c.keys_visible()) + 1, rd, c.dtype)
+            res = {}
+            for mode, rot in (("off", None), ("half_split", (cos, sin, False)),
+                              ("interleaved", (cos, sin, True))):
+                S, med, mn = run(c, inp, rot=rot)
+                res[mode] = (med, mn)
+            emit({"sweep": "rotary", "workload": label, "rotary_dim": rd, "splits": S,
+                  "off_ms": res["off"][0], "half_split_ms": res["half_split"][0],
+                  "interleaved_ms": res["interleaved"][0],
+                  "overhead_half_split": res["half_split"][0] / res["off"][0] - 1.0,
+                  "overhead_interleaved": res["interleaved"][0] / res["off"][0] - 1.0})
+            del inp
+            torch.cuda.empty_cache()
     elif name == "graph":
         # the same call eager and replayed from a HIP graph (launch overhead of
         # small, latency-bound calls); the buffers stay fixed, so one capture
@@ -324,7 +351,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
-    ap.add_argument("--sweep", choices=["copy", "decode", "gqa", "prefill", "unified", "graph",
+    ap.add_argument("--sweep", choices=["copy", "decode", "gqa", "prefill", "unified", "graph", "rotary",
                                         "multitoken"],
                     help="run a measurement sweep instead of the headline line")
     ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")

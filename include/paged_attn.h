@@ -52,7 +52,9 @@ typedef enum pa_status {
                              page (contiguous mode: one sequence's allocation) spans
                              2 GiB or more */
   PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than paged_attn_workspace_size */
-  PA_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+  PA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
+  PA_ERR_ALIGN = 7        /* a buffer read or written in 16-byte vectors (q, caches,
+                             k_new, v_new, out, rotary tables) is not 16-byte aligned */
 } pa_status;
 
 typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
@@ -84,6 +86,19 @@ typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
  *   - A row with no visible key gets out = 0 and softmax_lse = -inf.
  *   - Sequences with q_len_b = 0 (e.g. padded graph slots) write nothing.
  *   - Only the first cdiv(K_b, page_size) entries of a table row are read.
+ *   - Rotary embedding (rotary_cos != NULL): the small-page-size thread's
+ *     kernel fuses a rotary position embedding into the call; here it is the
+ *     standard RoPE rotation.  Every new token has the position K_b - q_len_b
+ *     + i (cache_seqlens[b] + i when k_new is given).  Its query row and its
+ *     new key row are rotated at that position before anything else; values
+ *     never are.  Pair j of a head row (elements (j, j + rotary_dim/2), or
+ *     (2j, 2j+1) when rotary_interleaved) becomes
+ *         (a cos - b sin, b cos + a sin),  cos = rotary_cos[pos][j],
+ *                                         sin = rotary_sin[pos][j];
+ *     elements from rotary_dim on are kept.  Arithmetic: the exact value
+ *     rounded to fp32, then to the element type (nearest even), so the stored
+ *     keys are bit-reproducible.  A position outside [0, rotary_rows) leaves
+ *     the row unrotated.
  *
  * Preconditions the host cannot check (device-resident metadata):
  *   q_len_b <= max_seqlen_q; K_b <= max_pages_per_seq * page_size (contiguous
@@ -123,6 +138,12 @@ typedef struct pa_fwd_args {
   float *softmax_lse;
   void *workspace;           /* device scratch, caller-owned; may be NULL if size is 0 */
   size_t workspace_bytes;
+  const void *rotary_cos;    /* [rotary_rows, rotary_dim / 2] dtype, or NULL: no rotary */
+  const void *rotary_sin;    /* same shape and type; NULL exactly when rotary_cos is */
+  int32_t rotary_dim;        /* with tables: a multiple of 16 in [16, head_dim]; else 0 */
+  int32_t rotary_interleaved;/* 0: pairs (j, j + rotary_dim / 2); 1: pairs (2j, 2j + 1) */
+  int32_t rotary_rows;       /* with tables: rows (positions) they hold, >= 1; else 0 */
+  int32_t reserved1;         /* must be 0 */
 } pa_fwd_args;
 
 /*
@@ -141,7 +162,9 @@ pa_status paged_attn_fwd(const pa_fwd_args *args, void *stream);
  * (or the contiguous cache).  Reads only the fields the append needs
  * (dtype, batch, total_q, max_seqlen_q, num_heads_kv, head_dim, page_size,
  * num_pages, max_pages_per_seq, contig_alloc, k_cache, v_cache, block_table,
- * cache_seqlens, cu_seqlens_q, k_new, v_new).  A bit copy: no rounding.
+ * cache_seqlens, cu_seqlens_q, k_new, v_new and the rotary fields).  A bit
+ * copy, except that with rotary tables each key row is first rotated at its
+ * position cache_seqlens[b] + i, as in paged_attn_fwd.
  */
 pa_status paged_kv_append(const pa_fwd_args *args, void *stream);
 

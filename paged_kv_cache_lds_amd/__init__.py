@@ -55,6 +55,9 @@ class _Args(ctypes.Structure):
         ("cu_seqlens_q", ctypes.c_void_p), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("softmax_lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("rotary_cos", ctypes.c_void_p), ("rotary_sin", ctypes.c_void_p),
+        ("rotary_dim", ctypes.c_int32), ("rotary_interleaved", ctypes.c_int32),
+        ("rotary_rows", ctypes.c_int32), ("reserved1", ctypes.c_int32),
     ]
 
 
@@ -113,9 +116,27 @@ def _check_dev(name, t, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _set_rotary(a: _Args, rotary_cos, rotary_sin, rotary_interleaved, dtype) -> None:
+    """Fill the rotary fields: tables [rows, rotary_dim / 2] in the element type."""
+    if (rotary_cos is None) != (rotary_sin is None):
+        raise ValueError("rotary_cos and rotary_sin go together")
+    if rotary_cos is None:
+        return
+    _check_dev("rotary_cos", rotary_cos, dtype)
+    _check_dev("rotary_sin", rotary_sin, dtype)
+    if rotary_cos.dim() != 2 or rotary_cos.shape != rotary_sin.shape:
+        raise ValueError("rotary_cos / rotary_sin must both be [rows, rotary_dim / 2]")
+    a.rotary_cos = _ptr(rotary_cos)
+    a.rotary_sin = _ptr(rotary_sin)
+    a.rotary_rows = rotary_cos.shape[0]
+    a.rotary_dim = 2 * rotary_cos.shape[1]
+    a.rotary_interleaved = int(bool(rotary_interleaved))
+
+
 def make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *, max_seqlen_q,
               max_seqlen_k=0, k_new=None, v_new=None, causal=False, num_splits=0,
-              softmax_scale=None, out=None, softmax_lse=None, workspace=None) -> _Args:
+              softmax_scale=None, out=None, softmax_lse=None, workspace=None, rotary_cos=None,
+              rotary_sin=None, rotary_interleaved=False) -> _Args:
     """Fill a ``pa_fwd_args`` from tensors (shapes read from the tensors)."""
     dt = q.dtype
     if dt not in _DTYPE_CODE:
@@ -160,6 +181,7 @@ def make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *, 
     a.softmax_lse = _ptr(softmax_lse)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _set_rotary(a, rotary_cos, rotary_sin, rotary_interleaved, dt)
     return a
 
 
@@ -179,13 +201,17 @@ def _stream_handle(stream) -> int:
 def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *,
                    max_seqlen_q: int, max_seqlen_k: int = 0, k_new=None, v_new=None,
                    causal: bool = False, num_splits: int = 0, softmax_scale=None, out=None,
-                   softmax_lse=None, workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                   softmax_lse=None, workspace=None, rotary_cos=None, rotary_sin=None,
+                   rotary_interleaved: bool = False,
+                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged attention forward (with optional in-call append of k_new/v_new).
 
     q [total_q, Hq, D]; k_cache/v_cache [num_pages, page_size, Hkv, D] (or
     [batch, alloc, Hkv, D] with ``block_table=None``); block_table [batch,
     width] int32; cache_seqlens [batch] int32; cu_seqlens_q [batch+1] int32.
     ``max_seqlen_q`` must bound every q_len on the host side (no device read).
+    ``rotary_cos`` / ``rotary_sin`` [rows, rotary_dim / 2] (element type) turn
+    on the fused rotary embedding of q and k_new.
     Returns (out [total_q, Hq, D], softmax_lse [total_q, Hq] fp32).
     """
     if out is None:
@@ -196,7 +222,8 @@ def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q
                      max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, k_new=k_new,
                      v_new=v_new, causal=causal, num_splits=num_splits,
                      softmax_scale=softmax_scale, out=out, softmax_lse=softmax_lse,
-                     workspace=workspace)
+                     workspace=workspace, rotary_cos=rotary_cos, rotary_sin=rotary_sin,
+                     rotary_interleaved=rotary_interleaved)
     if workspace is None:
         need = paged_attn_workspace_size(args)
         if need > 0:
@@ -210,8 +237,10 @@ def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q
 
 
 def paged_kv_append(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, k_new, v_new, *,
-                    max_seqlen_q: int, stream=None) -> None:
-    """Write k_new/v_new rows at positions cache_seqlens[b] + i (bit copy)."""
+                    max_seqlen_q: int, rotary_cos=None, rotary_sin=None,
+                    rotary_interleaved: bool = False, stream=None) -> None:
+    """Write k_new/v_new rows at positions cache_seqlens[b] + i (bit copy; keys
+    rotated at those positions first when rotary tables are given)."""
     dt = k_cache.dtype
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
                     ("v_new", v_new)):
@@ -237,6 +266,7 @@ def paged_kv_append(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, 
     a.cu_seqlens_q = _ptr(cu_seqlens_q)
     a.k_new = _ptr(k_new)
     a.v_new = _ptr(v_new)
+    _set_rotary(a, rotary_cos, rotary_sin, rotary_interleaved, dt)
     st = _lib().paged_kv_append(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream)))
     if st != 0:
         raise PagedAttnError(st, "paged_kv_append")

@@ -35,6 +35,7 @@ struct FwdParams {
   int appended, causal, num_splits;
   float scale_log2;    // softmax scale * log2(e)
   int all_decode;      // host knows every sequence has q_len * group <= 16
+  Rotary rot;          // rotary embedding of q (rot.cos == nullptr: none)
 };
 
 struct AppendParams {
@@ -46,15 +47,18 @@ struct AppendParams {
   const uint16_t *k_new;
   const uint16_t *v_new;
   int batch, total_q, hkv, head_dim, tokens_per_block;
+  Rotary rot;          // rotary embedding of the new keys (rot.cos == nullptr: none)
 };
 
 // ---------------------------------------------------------------------------
 // Append (vLLM's reshape_and_cache; the in-call k=/v= of flash-attention's
 // paged cache): new row i of sequence b goes to logical position
-// cache_seqlens[b] + i.  Grid (cdiv(max_seqlen_q, tokens_per_block), batch);
-// each thread moves 16-byte vectors.  Targets whose page id is outside the
-// pool (a caller precondition violation) are skipped, never written.
+// cache_seqlens[b] + i, its key rotated for that position when a rotary table
+// is given.  Grid (cdiv(max_seqlen_q, tokens_per_block), batch); each thread
+// moves 16-byte vectors.  Targets whose page id is outside the pool (a caller
+// precondition violation) are skipped, never written.
 // ---------------------------------------------------------------------------
+template <int DT>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
   const int b = blockIdx.y;
   const int cu_b = p.cu_seqlens_q[b];
@@ -77,7 +81,14 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
     const long src = ((long)(cu_b + i) * vec_per_row + v) * 8;
     const long dst = (prow * vec_per_row + v) * 8;
     if (which == 0) {
-      store16(p.k_cache + dst, load16(p.k_new + src));
+      u32x4 k[1] = {load16(p.k_new + src)};
+      if (p.rot.cos != nullptr) {
+        const int e0 = (v % (p.head_dim >> 3)) * 8;   // offset inside the head row
+        RotFetch<1> f;
+        rot_fetch(p.rot, p.k_new + src - e0, e0, 0, L + i, f);
+        rot_apply<DT>(p.rot, e0, 0, L + i, k, f);
+      }
+      store16(p.k_cache + dst, k[0]);
     } else {
       store16(p.v_cache + dst, load16(p.v_new + src));
     }

@@ -78,6 +78,14 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
     for (int ds = 0; ds < DS; ++ds)
       qf[ds] = row_ok ? load16(qrow + (ds * 4 + lg) * 8) : u32x4{0u, 0u, 0u, 0u};
   }
+  // fused rotary embedding of the query row, at the token's position
+  // K_b - q_len + tok: its operands are fetched with the row, and applied once
+  // the first tile's loads are out (see below)
+  const bool rot_q = p.rot.cos != nullptr;
+  const int rot_pos = row_ok ? si.K_b - si.q_len + tok : -1;
+  RotFetch<DS> rotf;
+  if (rot_q)
+    rot_fetch(p.rot, p.q + ((long)(si.cu_b + tok) * p.hq + h) * D, lg * 8, 32, rot_pos, rotf);
 
   const CacheGeom &cg = p.geom;
   const bool paged = cg.table != nullptr;
@@ -246,6 +254,7 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
     int ids_a = load_ids(w_begin);
     int ids_b = load_ids(w_begin + 1);
     issue(w_begin, ka, va_, ids_a);
+    if (rot_q) rot_apply<DT>(p.rot, lg * 8, 32, rot_pos, qf, rotf);
     ids_a = load_ids(w_begin + 2);
     issue(w_begin + 1, kb_, vb_, ids_b);
     ids_b = load_ids(w_begin + 3);

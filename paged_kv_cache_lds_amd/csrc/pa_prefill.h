@@ -81,6 +81,14 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     for (int ds = 0; ds < QS; ++ds)
       qf[ds] = row_ok ? load16(qrow + ds * 16 + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
   }
+  // fused rotary embedding of the query row, at the token's position
+  // K_b - q_len + tok: its table entries are fetched with the row and applied
+  // after the prologue's wait, so their latency hides behind the first tiles'
+  // loads
+  const bool rot_q = p.rot.cos != nullptr;
+  const int rot_pos = row_ok ? si.K_b - si.q_len + tok : -1;
+  u32x4 rot_c[QS / 2], rot_s[QS / 2];
+  if (rot_q) rot_fetch_split<QS>(p.rot, rot_pos, hh, rot_c, rot_s);
 
   // ---- LDS layout ----
   // LDS serves 256 bytes a clock in 64 four-byte banks: 16 lanes of a 16-byte
@@ -397,6 +405,7 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     }
   }
   wait_then_barrier<0>();
+  if (rot_q) rot_apply_split<DT, QS>(p.rot, rot_pos, hh, qf, rot_c, rot_s);
   {
     f32x16 s0;
     qk(k_slot[0], s0);

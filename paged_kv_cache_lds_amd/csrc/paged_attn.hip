@@ -61,6 +61,27 @@ pa_status validate(const pa_fwd_args *a, bool append_only, bool sizes_only = fal
                      a->cache_seqlens == nullptr || a->cu_seqlens_q == nullptr))
     return PA_ERR_NULL;
   if ((a->k_new == nullptr) != (a->v_new == nullptr)) return PA_ERR_NULL;
+  // rotary embedding: both tables or neither; the pairs must fill whole
+  // 16-byte chunks (rotary_dim a multiple of 16)
+  if (a->reserved1 != 0) return PA_ERR_SHAPE;
+  if ((a->rotary_cos == nullptr) != (a->rotary_sin == nullptr)) return PA_ERR_NULL;
+  if (a->rotary_cos == nullptr) {
+    if (a->rotary_dim != 0 || a->rotary_rows != 0 || a->rotary_interleaved != 0)
+      return PA_ERR_SHAPE;
+  } else {
+    if (a->rotary_dim < 16 || a->rotary_dim > a->head_dim || a->rotary_dim % 16 != 0)
+      return PA_ERR_SHAPE;
+    if (a->rotary_rows < 1 || (a->rotary_interleaved != 0 && a->rotary_interleaved != 1))
+      return PA_ERR_SHAPE;
+  }
+  if (!sizes_only) {
+    // every buffer the kernels move in 16-byte vectors
+    const void *vec[] = {a->k_cache, a->v_cache, a->k_new, a->v_new, a->rotary_cos,
+                         a->rotary_sin, append_only ? nullptr : a->q,
+                         append_only ? nullptr : a->out};
+    for (const void *v : vec)
+      if ((reinterpret_cast<uintptr_t>(v) & 15u) != 0) return PA_ERR_ALIGN;
+  }
   if (append_only) {
     if (a->k_new == nullptr) return PA_ERR_NULL;
     return PA_OK;
@@ -133,6 +154,16 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
   return pl;
 }
 
+pa::Rotary rotary_of(const pa_fwd_args *a) {
+  pa::Rotary r;
+  r.cos = static_cast<const uint16_t *>(a->rotary_cos);
+  r.sin = static_cast<const uint16_t *>(a->rotary_sin);
+  r.rows = a->rotary_rows;
+  r.rdim = a->rotary_cos != nullptr ? a->rotary_dim : 0;
+  r.interleaved = a->rotary_interleaved;
+  return r;
+}
+
 pa::CacheGeom geom_of(const pa_fwd_args *a) {
   pa::CacheGeom g;
   g.table = a->block_table;
@@ -157,11 +188,15 @@ pa_status launch_append(const pa_fwd_args *a, hipStream_t stream) {
   p.total_q = a->total_q;
   p.hkv = a->num_heads_kv;
   p.head_dim = a->head_dim;
+  p.rot = rotary_of(a);
   const int vec_per_row = a->num_heads_kv * a->head_dim / 8;
   p.tokens_per_block = std::max(1, 1024 / (2 * vec_per_row));
   dim3 grid((unsigned)cdiv(a->max_seqlen_q, p.tokens_per_block), (unsigned)a->batch);
   if (grid.y > 65535u) return PA_ERR_SHAPE;
-  hipLaunchKernelGGL(pa::kv_append_kernel, grid, dim3(kThreads), 0, stream, p);
+  if (a->dtype == PA_BF16)
+    hipLaunchKernelGGL(pa::kv_append_kernel<pa::kBF16>, grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(pa::kv_append_kernel<pa::kF16>, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -193,6 +228,7 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
                                              : 1.0f / std::sqrt((float)a->head_dim);
   p.scale_log2 = scale * pa::kLog2e;
   p.all_decode = pl.all_decode;
+  p.rot = rotary_of(a);
   if (pl.grid > 0x7fffffffL) return PA_ERR_SHAPE;
   if (pl.all_decode)
     hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(kThreads),
@@ -300,6 +336,7 @@ const char *paged_attn_status_string(int32_t status) {
     case PA_ERR_UNSUPPORTED: return "head_dim or page size not supported (head_dim 64/128, page size a power of two in [16, 256])";
     case PA_ERR_WORKSPACE: return "workspace missing or smaller than paged_attn_workspace_size";
     case PA_ERR_HIP: return "a HIP launch or runtime call failed";
+    case PA_ERR_ALIGN: return "a buffer moved in 16-byte vectors is not 16-byte aligned";
     default: return "unknown status";
   }
 }

@@ -81,6 +81,19 @@ def call_fwd(a):
     (dict(batch=0), 2), (dict(causal=2), 2), (dict(reserved0=1), 2),
     (dict(block_table=None, contig_alloc=0), 2),
     (dict(num_splits=4), 5),                       # splits need a workspace
+    # rotary embedding fields
+    (dict(rotary_cos=0x3000, rotary_dim=32, rotary_rows=8), 1),           # cos without sin
+    (dict(rotary_dim=32), 2), (dict(rotary_rows=4), 2), (dict(rotary_interleaved=1), 2),
+    (dict(rotary_cos=0x3000, rotary_sin=0x4000, rotary_dim=8, rotary_rows=8), 2),
+    (dict(rotary_cos=0x3000, rotary_sin=0x4000, rotary_dim=24, rotary_rows=8), 2),
+    (dict(rotary_cos=0x3000, rotary_sin=0x4000, rotary_dim=128, rotary_rows=8), 2),  # > head_dim
+    (dict(rotary_cos=0x3000, rotary_sin=0x4000, rotary_dim=32, rotary_rows=0), 2),
+    (dict(rotary_cos=0x3000, rotary_sin=0x4000, rotary_dim=32, rotary_rows=8,
+          rotary_interleaved=2), 2),
+    (dict(reserved1=1), 2),
+    # 16-byte alignment of every buffer moved in 16-byte vectors
+    (dict(q=0x1008), 7), (dict(out=0x1002), 7), (dict(k_cache=0x1004), 7),
+    (dict(rotary_cos=0x3008, rotary_sin=0x4000, rotary_dim=32, rotary_rows=8), 7),
 ])
 def test_host_validation_codes(over, code):
     assert call_fwd(valid_args(**over)) == code
@@ -104,7 +117,7 @@ def test_workspace_size_and_splits_for_are_host_only():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         assert pa.paged_attn_status_string(code) != "unknown status"
     assert pa.paged_attn_status_string(99) == "unknown status"
 

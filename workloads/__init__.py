@@ -257,3 +257,26 @@ def unified_varlen(nq, heads=32, head_dim=128, prefix=0, seed=4000) -> Case:
                 cache_seqlens=[prefix] + dec, num_heads_q=heads, num_heads_kv=heads,
                 head_dim=head_dim, dtype="f16", page_size=16, append=True, causal=True,
                 seed=seed + nq + heads)
+
+
+def rotary_tables(rows: int, rotary_dim: int, dtype="f16", device="cuda", base=10000.0,
+                  kind="angles", seed=0):
+    """cos / sin tables [rows, rotary_dim / 2] in the storage dtype, inputs of
+    the fused rotary embedding.  kind "angles": cos / sin of m * base^(-2i /
+    rotary_dim) for position m and pair i (evaluated in fp64, rounded once);
+    kind "random": seeded uniform [-1, 1) values (the rotation formula does not
+    need a true rotation, and random tables exercise every table element)."""
+    half = rotary_dim // 2
+    if kind == "angles":
+        theta = base ** (-2.0 * np.arange(half, dtype=np.float64) / rotary_dim)
+        ang = np.arange(rows, dtype=np.float64)[:, None] * theta[None, :]
+        c, s = np.cos(ang), np.sin(ang)
+    elif kind == "random":
+        rng = np.random.default_rng(seed)
+        c = rng.uniform(-1.0, 1.0, (rows, half))
+        s = rng.uniform(-1.0, 1.0, (rows, half))
+    else:
+        raise ValueError(kind)
+    td = TORCH_DTYPE[dtype]
+    return (torch.from_numpy(c).to(td).to(device).contiguous(),
+            torch.from_numpy(s).to(td).to(device).contiguous())
