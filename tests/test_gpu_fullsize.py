@@ -1,0 +1,160 @@
+"""GPU parity at the workloads' full sizes, in the launch configurations that
+bench.py times, on sampled rows the oracle computes one token at a time.
+
+For a sampled new token i of sequence b (q_len n, cache length L, K_b keys
+visible to the call), the oracle gets that token's query rows alone, over the
+sequence's first K_b - n + i + 1 keys (bottom-right causal alignment) laid
+out as one contiguous sequence: cached keys are read from the pool before the
+call through the sequence's page list, new keys straight from k_new.  So the
+oracle shares nothing with the GPU's append or page walk.  The GPU call is
+the whole call (append, heuristic split budget, combine); its appended slots
+of the sampled sequences are checked bit-exactly against k_new / v_new.
+Bars as in the other parity tests: max |out - oracle| <= 2e-3, |lse - oracle|
+<= 1e-4 |oracle| + 1e-6.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_lds_amd as pa
+import workloads as wl
+from workloads import host, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-3
+LSE_REL = 1e-4
+LSE_ABS = 1e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    assert pa._lib() is not None
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def pages_of(inp, b, n_keys):
+    """Physical page ids holding keys 0 .. n_keys-1 of sequence b."""
+    P = inp.case.page_size
+    return np.asarray(inp.pages_of[b][: -(-n_keys // P)], dtype=np.int64)
+
+
+def cached_rows(inp, b, L):
+    """K and V rows 0 .. L-1 of sequence b as [L, Hkv, D] uint16, read from the
+    pool through its page list (paged) or its allocation (contiguous)."""
+    if L == 0:
+        shape = (0,) + tuple(inp.k_cache.shape[2:])
+        return np.zeros(shape, np.uint16), np.zeros(shape, np.uint16)
+    if inp.block_table is None:
+        return host(inp.k_cache[b, :L]), host(inp.v_cache[b, :L])
+    P = inp.case.page_size
+    idx = torch.from_numpy(pages_of(inp, b, L)).to(inp.k_cache.device)
+    k = host(inp.k_cache.index_select(0, idx)).reshape((-1,) + tuple(inp.k_cache.shape[2:]))
+    v = host(inp.v_cache.index_select(0, idx)).reshape((-1,) + tuple(inp.v_cache.shape[2:]))
+    return k[:L], v[:L]
+
+
+def run_fullsize(case, samples, num_splits=0, max_seqlen_k=None, causal=None):
+    """samples: {sequence: [token indices]}; one whole GPU call, then the
+    oracle per sampled token."""
+    say(f"case {case.name} seed {case.seed} (full size)")
+    inp = make_inputs(case, "cuda")
+    causal = case.causal if causal is None else causal
+    cu = host(inp.cu_seqlens_q)
+    # everything the oracle needs, taken before the call
+    before = {b: cached_rows(inp, b, case.cache_seqlens[b]) for b in samples}
+    qh = {b: host(inp.q[int(cu[b]):int(cu[b + 1])]) for b in samples}
+    knh = {b: host(inp.k_new[int(cu[b]):int(cu[b + 1])]) for b in samples} if case.append else {}
+    vnh = {b: host(inp.v_new[int(cu[b]):int(cu[b + 1])]) for b in samples} if case.append else {}
+    say("  gpu call")
+    out, lse = pa.paged_attn_fwd(
+        inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens, inp.cu_seqlens_q,
+        max_seqlen_q=inp.max_seqlen_q,
+        max_seqlen_k=inp.max_seqlen_k if max_seqlen_k is None else max_seqlen_k,
+        k_new=inp.k_new, v_new=inp.v_new, causal=causal, num_splits=num_splits)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for b, toks in samples.items():
+        L = case.cache_seqlens[b]
+        n = int(cu[b + 1] - cu[b])
+        kb, vb = before[b]
+        if case.append:
+            # appended slots, bit for bit
+            ka, va = cached_rows(inp, b, L + n)
+            assert np.array_equal(ka[:L], kb) and np.array_equal(va[:L], vb), "cached rows changed"
+            assert np.array_equal(ka[L:], knh[b]) and np.array_equal(va[L:], vnh[b]), \
+                f"sequence {b}: appended rows differ"
+            kb = np.concatenate([kb, knh[b]])
+            vb = np.concatenate([vb, vnh[b]])
+        K_b = L + (n if case.append else 0)
+        for i in toks:
+            vis = (K_b - n + i + 1) if causal else K_b
+            vis = max(0, min(vis, K_b))
+            kc = np.zeros((1, max(vis, 1)) + kb.shape[1:], np.uint16)
+            vc = np.zeros((1, max(vis, 1)) + vb.shape[1:], np.uint16)
+            kc[0, :vis] = kb[:vis]
+            vc[0, :vis] = vb[:vis]
+            ref_o, ref_l = oracle.attention(qh[b][i:i + 1], kc, vc, None, np.array([vis], np.int32),
+                                            np.array([0, 1], np.int32), dtype=case.dtype,
+                                            appended=False, causal=False)
+            row = int(cu[b]) + i
+            o = out[row].float().cpu().numpy().astype(np.float64)
+            l = lse[row].cpu().numpy().astype(np.float64)
+            err = np.abs(o - ref_o[0]).max()
+            worst = max(worst, err)
+            assert err <= OUT_TOL, f"seq {b} token {i}: out err {err}"
+            fin = ~np.isneginf(ref_l[0])
+            assert np.array_equal(np.isneginf(l), ~fin), f"seq {b} token {i}: -inf pattern"
+            assert (np.abs(l[fin] - ref_l[0][fin]) <= LSE_REL * np.abs(ref_l[0][fin]) + LSE_ABS).all(), \
+                f"seq {b} token {i}: lse"
+    say(f"  max out err {worst:.3g}")
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_mha_decode_b256_ctx4096_with_append():
+    # the bench step: append one token per sequence, heuristic split budget
+    c = wl.mha_decode(256, 4096, append=True)
+    run_fullsize(c, {0: [0], 77: [0], 255: [0]}, causal=False)
+
+
+@pytest.mark.parametrize("P", [16, 256])
+def test_mha_decode_batch_sweep_corner(P):
+    # the decode sweep's largest point at both page sizes (attention only)
+    c = wl.mha_decode(256, 4096, page_size=P)
+    run_fullsize(c, {3: [0], 200: [0]}, causal=False)
+
+
+@pytest.mark.parametrize("paged", [True, False])
+def test_gqa_long_split_allocation_bound(paged):
+    # batch 8, 64/8 heads, lengths in [2048, 32768] inside a 131072-token
+    # allocation; heuristic split budget from the allocation bound
+    c = wl.gqa_long_split(paged=paged)
+    longest = int(np.argmax(c.cache_seqlens))
+    run_fullsize(c, {longest: [0], 0: [0]})
+
+
+@pytest.mark.parametrize("prefix", ["zero", "uniform"])
+def test_causal_prefill_4x2048(prefix):
+    c = wl.causal_prefill_append(2048, prefix)
+    run_fullsize(c, {0: [0, 255, 256, 1000, 2047], 3: [31, 2046]})
+
+
+def test_causal_prefill_4x170():
+    c = wl.causal_prefill_append(170, "uniform")
+    run_fullsize(c, {1: [0, 100, 169]})
+
+
+@pytest.mark.parametrize("nq,heads,hd", [(100, 32, 128), (500, 32, 128), (1000, 32, 128),
+                                         (100, 12, 64), (1000, 12, 64)])
+def test_unified_varlen_full(nq, heads, hd):
+    c = wl.unified_varlen(nq, heads=heads, head_dim=hd)
+    run_fullsize(c, {0: [0, nq // 2, nq - 1], 1: [0], 40: [0], 64: [0]})
