@@ -132,6 +132,7 @@ def sweep(name, reps, out_path):
     """Measurement sweeps over the workload families (one JSON object per
     point, appended to `out_path`); each point reports median / min call time
     and the fraction of its roofline."""
+    import numpy as np
     import torch
 
     import paged_kv_cache_lds_amd as pa
@@ -232,6 +233,22 @@ def sweep(name, reps, out_path):
                       "frac": by / med / 1e6 / HBM_PEAK_GBS})
             del inp
             torch.cuda.empty_cache()
+        # the same heads and allocation with short live lengths (64..512): the
+        # host sizes the budget from the allocation, the device caps splits
+        # at >= 8 key tiles each
+        rng = np.random.default_rng(2500)
+        lens = [int(x) for x in rng.integers(64, 512, size=8, endpoint=True)]
+        c = wl.Case(**{**wl.gqa_long_split(True).__dict__, "name": "gqa_short_in_long_alloc",
+                       "cache_seqlens": lens, "seed": 2500})
+        inp = wl.make_inputs(c, "cuda")
+        by = algorithmic_bytes(c)
+        for s in (0, 1, 8, 32, 128):
+            S, med, mn = run(c, inp, num_splits=s)
+            emit({"sweep": "gqa", "paged": True, "lengths": "64..512", "splits": S,
+                  "heuristic": "alloc" if s == 0 else None, "ms": med, "ms_min": mn,
+                  "GBps": by / med / 1e6, "frac": by / med / 1e6 / HBM_PEAK_GBS})
+        del inp
+        torch.cuda.empty_cache()
     elif name == "prefill":
         for nq, prefix in ((170, "zero"), (170, "uniform"), (2048, "zero"), (2048, "uniform"),
                            (8192, "zero")):

@@ -115,10 +115,16 @@ __device__ inline SeqInfo seq_info(const FwdParams &p, int b) {
 // here, with the real lengths in hand, every decode sequence keeps one unit
 // and the remaining budget is shared in proportion to its key tiles, so long
 // sequences get more splits than short ones (cache_seqlens never travels to
-// the host).  A pure function of the lengths: every workgroup agrees on it.
+// the host).  No split gets fewer than kMinSplitTiles key tiles (two per
+// wave): a cache allocated far beyond its live length, or a forced budget
+// larger than the keys can use, leaves the rest of the budget unused instead
+// of paying partial results for near-empty splits.  A pure function of the
+// lengths: every workgroup agrees on it.
+constexpr long kMinSplitTiles = 8;
 __device__ inline int seq_splits(long extra_budget, long tiles_b, long total_tiles) {
   if (extra_budget <= 0 || total_tiles <= 0) return 1;
-  const long s = 1 + (extra_budget * tiles_b) / total_tiles;
+  long s = 1 + (extra_budget * tiles_b) / total_tiles;
+  s = min(s, max(1L, tiles_b / kMinSplitTiles));
   return (int)min(s, (long)kMaxSplits);
 }
 

@@ -124,6 +124,19 @@ def test_gqa_split_sweep(paged):
     run_parity(reduced_gqa(paged), splits=(None, 1, 2, 4, 8, 16, 32, 64, 128))
 
 
+@pytest.mark.parametrize("lo,hi", [(1, 300), (64, 512)])
+def test_gqa_short_lengths_in_a_large_allocation(lo, hi):
+    # live lengths far below the 131072-token allocation the host sizes from:
+    # the device keeps every split at >= 8 key tiles, so forced budgets far
+    # above what the keys can use leave units empty instead of near-empty
+    rng = np.random.default_rng(2400 + lo)
+    lens = [int(x) for x in rng.integers(lo, hi, 8, endpoint=True)]
+    c = Case(name=f"gqa_short_{lo}_{hi}", q_lens=[1] * 8, cache_seqlens=lens, num_heads_q=64,
+             num_heads_kv=8, head_dim=128, dtype="bf16", page_size=16, table_width=131072 // 16,
+             causal=True, seed=2400 + lo, max_seqlen_k_hint=131072)
+    run_parity(c, splits=(None, 1, 8, 32, 128))
+
+
 def test_gqa_split_sharp_softmax():
     run_parity(reduced_gqa(True, values="normal3", seed=2200), splits=(None, 1, 5))
 
