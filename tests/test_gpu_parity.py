@@ -146,6 +146,57 @@ def test_causal_prefill_append(nq, prefix):
     run_parity(wl.causal_prefill_append(nq, prefix))
 
 
+@pytest.mark.parametrize("dtype,P,hq,hkv,hd,prefix", [
+    ("bf16", 16, 32, 32, 128, "uniform"),     # bf16 prefill (probabilities as hi + lo)
+    ("f16", 256, 32, 32, 128, "uniform"),     # one page holds a whole tile row range
+    ("f16", None, 32, 32, 128, "uniform"),    # contiguous cache
+    ("bf16", 16, 64, 8, 128, "uniform"),      # GQA prefill: 8 q heads per kv head
+    ("f16", 16, 12, 12, 64, "zero"),          # head_dim 64 prefill
+    ("bf16", 32, 48, 16, 64, "uniform"),      # GQA group 3: a token's rows straddle units
+])
+def test_causal_prefill_variants(dtype, P, hq, hkv, hd, prefix):
+    rng = np.random.default_rng(3100 + hq + hd)
+    L = [0] * 3 if prefix == "zero" else [int(x) for x in rng.integers(0, 300, 3, endpoint=True)]
+    nq = [130, 77, 301]
+    c = Case(name=f"prefill_{dtype}_P{P}_{hq}x{hkv}x{hd}", q_lens=nq, cache_seqlens=L,
+             num_heads_q=hq, num_heads_kv=hkv, head_dim=hd, dtype=dtype, page_size=P,
+             contig_alloc=0 if P else max(a + b for a, b in zip(L, nq)) + 5, append=True,
+             causal=True, seed=3100 + hq + hd)
+    run_parity(c)
+
+
+@pytest.mark.parametrize("kind", ["prefill", "unified", "decode"])
+def test_non_causal_and_softmax_scale(kind):
+    # non-causal attention over every key (new rows included) and a caller
+    # softmax scale, through each kernel
+    if kind == "prefill":
+        c = Case(name="noncausal_prefill", q_lens=[130, 40], cache_seqlens=[50, 260], num_heads_q=16,
+                 num_heads_kv=4, head_dim=128, dtype="f16", page_size=16, append=True,
+                 causal=False, seed=3300)
+    elif kind == "unified":
+        c = Case(name="noncausal_unified", q_lens=[90, 1, 1, 3], cache_seqlens=[17, 400, 0, 33],
+                 num_heads_q=8, num_heads_kv=8, head_dim=64, dtype="bf16", page_size=32,
+                 append=True, causal=False, seed=3301)
+    else:
+        c = Case(name="noncausal_decode", q_lens=[2, 1, 4], cache_seqlens=[300, 45, 1000],
+                 num_heads_q=8, num_heads_kv=2, head_dim=128, dtype="f16", page_size=16,
+                 append=True, causal=False, seed=3302)
+    say(f"case {c.name} seed {c.seed}")
+    inp = make_inputs(c, "cuda")
+    kc0, vc0 = host(inp.k_cache), host(inp.v_cache)
+    scale = 0.37
+    ref_out, ref_lse, ref_kc, ref_vc = oracle.paged_attention(
+        host(inp.q), kc0, vc0, host(inp.block_table), host(inp.cache_seqlens),
+        host(inp.cu_seqlens_q), host(inp.k_new), host(inp.v_new), dtype=c.dtype, causal=False,
+        scale=scale)
+    for s in (None, 3):
+        inp.k_cache.copy_(torch.from_numpy(kc0.view(np.int16)).view(inp.k_cache.dtype))
+        inp.v_cache.copy_(torch.from_numpy(vc0.view(np.int16)).view(inp.v_cache.dtype))
+        out, lse = gpu_call(inp, num_splits=s, softmax_scale=scale)
+        check_against_oracle(out, lse, ref_out, ref_lse, f"{c.name} S={s}")
+        assert np.array_equal(host(inp.k_cache), ref_kc) and np.array_equal(host(inp.v_cache), ref_vc)
+
+
 def test_causal_prefill_sharp_softmax():
     c = wl.causal_prefill_append(100, "uniform")
     c.values = "normal3"
