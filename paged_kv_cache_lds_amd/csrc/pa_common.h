@@ -154,6 +154,97 @@ __device__ inline int block_inclusive_scan(int x, int *s_wsum, int &total) {
   return before + x;
 }
 
+// Decode units in longest-first order.  Workgroups are dispatched in grid
+// order and a free slot takes the next one, so the order of the units is the
+// schedule: with sequences of mixed lengths, the long ones' units should go
+// first, or they start late and finish last (the tail of a varlen batch).
+// Decode units are therefore enumerated by decreasing key tiles per unit
+// (ties by sequence index), the splits of one sequence consecutive.  Ranks
+// come from comparing every decode sequence with every other in LDS; batches
+// beyond kOrderMax sequences keep index order.  Already ordered batches
+// (equal lengths included) skip the comparisons.  The caller decides where
+// this applies (a null order keeps index order).
+constexpr int kOrderMax = 1024;
+struct DecodeOrder {
+  int key[kOrderMax];   // by sequence: key tiles per decode unit, -1 without decode units
+  int seq[kOrderMax];   // by rank: the sequence
+  int cnt[kOrderMax];   // by rank: its decode units (splits); 0 past the last rank
+};
+
+// The decode unit(s) `first` .. `first + kDecPerWg - 1` (per kv head, in the
+// order above) into s_found, as in locate_unit's second pass.  Every thread of
+// the workgroup takes part; barriers are uniform.
+template <int NT, int kDecPerWg>
+__device__ inline void find_decode_ordered(const FwdParams &p, long first, long extra,
+                                           long total_tiles, DecodeOrder &o, int *s_wsum,
+                                           int *s_found) {
+  constexpr int PER = kOrderMax / NT;
+  const int tid = threadIdx.x;
+  int my_key[PER], my_cnt[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = tid + i * NT;
+    int key = -1, cnt = 0;
+    if (s < p.batch) {
+      const SeqInfo si = seq_info(p, s);
+      const int rows = si.q_len * p.group;
+      if (rows > 0 && (p.all_decode || rows <= kDecodeRows)) {
+        const long tiles = decode_tiles(si.K_b);
+        cnt = seq_splits(extra, tiles, total_tiles);
+        key = (int)((tiles + cnt - 1) / cnt);
+      }
+      o.key[s] = key;
+      o.cnt[s] = 0;
+    }
+    my_key[i] = key;
+    my_cnt[i] = cnt;
+  }
+  if (tid < 3 * kDecPerWg) s_found[tid] = -1;
+  __syncthreads();
+  bool unordered = false;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = tid + i * NT;
+    if (s + 1 < p.batch && my_key[i] < o.key[s + 1]) unordered = true;
+  }
+  unordered = __syncthreads_or(unordered);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = tid + i * NT;
+    if (my_key[i] < 0) continue;
+    int r = s;   // ordered: decode sequences first, in index order
+    if (unordered) {
+      r = 0;
+      for (int s2 = 0; s2 < p.batch; ++s2) {
+        const int k2 = o.key[s2];
+        r += (k2 > my_key[i]) | ((k2 == my_key[i]) & (s2 < s));
+      }
+    }
+    o.seq[r] = s;
+    o.cnt[r] = my_cnt[i];
+  }
+  __syncthreads();
+  long carry = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += NT) {
+    const int r = c0 + tid;
+    const int units = r < p.batch ? o.cnt[r] : 0;
+    int total;
+    const long incl = carry + block_inclusive_scan<NT / 64>(units, s_wsum, total);
+    const long excl = incl - units;
+    for (int h = 0; h < kDecPerWg; ++h) {
+      const long want = first + h;
+      if (units > 0 && want >= excl && want < incl) {
+        s_found[3 * h] = o.seq[r];
+        s_found[3 * h + 1] = (int)(want - excl);
+        s_found[3 * h + 2] = units;
+      }
+    }
+    carry += total;
+    __syncthreads();
+    if (s_found[3 * (kDecPerWg - 1)] >= 0) break;   // the last one sought is found
+  }
+}
+
 // Work mapping.  Units per kv head, prefill units first: a sequence whose
 // packed rows (q_len * group) exceed one 16-row decode unit gets
 // cdiv(rows, kPrefillRows) prefill units, heaviest (last, under the causal
@@ -170,7 +261,7 @@ struct UnitInfo {
 
 template <int NT, int kDecPerWg>
 __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool &decode,
-                                   int *s_wsum, int *s_found) {
+                                   int *s_wsum, int *s_found, DecodeOrder *order) {
   const int tid = threadIdx.x;
   const int half = kDecPerWg == 2 ? tid / (NT / 2) : 0;
   const int S = p.num_splits;
@@ -210,6 +301,15 @@ __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool
   // pass 2: prefix over the units of our kind, find ours (one per half)
   const bool pre_wg = wg < n_pre;
   const long first = pre_wg ? wg : (wg - n_pre) * kDecPerWg;   // first unit index sought
+  if (!pre_wg && p.batch <= kOrderMax && order != nullptr) {
+    find_decode_ordered<NT, kDecPerWg>(p, first, extra, total_tiles, *order, s_wsum, s_found);
+    const int slot = 3 * half;
+    u.b = s_found[slot];
+    u.off = s_found[slot + 1];
+    u.splits = s_found[slot + 2];
+    decode = true;
+    return u.b >= 0;
+  }
   if (tid < 6) s_found[tid] = -1;
   __syncthreads();
   long carry = 0;
