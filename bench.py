@@ -277,9 +277,11 @@ def sweep(name, reps, out_path):
                 pi = wl.make_inputs(pre, "cuda")
                 _, dmed, _ = run(dec, di)
                 _, pmed, _ = run(pre, pi)
+                dby = algorithmic_bytes(dec)
                 emit({"sweep": "unified", "nq": nq, "heads": heads, "head_dim": hd, "splits": S,
                       "ms": med, "ms_min": mn, "roofline_ms": t_roof, "frac": t_roof / med,
-                      "two_call_ms": dmed + pmed})
+                      "two_call_ms": dmed + pmed, "decode_only_ms": dmed,
+                      "decode_only_frac": dby / (HBM_PEAK_GBS * 1e9) * 1e3 / dmed})
                 del inp, di, pi
                 torch.cuda.empty_cache()
     elif name == "multitoken":
