@@ -347,6 +347,40 @@ def test_varlen_equals_one_call_per_sequence():
         assert torch.equal(o1, out[s:e]) and torch.equal(l1, lse[s:e]), f"sequence {b}"
 
 
+@pytest.mark.parametrize("batch", [40, 1024, 1030])
+def test_decode_varlen_unit_order(batch):
+    # decode-only batches with one unit per sequence run their units longest
+    # first (up to 1024 sequences; index order past that): unsorted lengths
+    # with ties and (0, 0) padding slots; results must not depend on the order
+    rng = np.random.default_rng(5200 + batch)
+    lens = [int(x) for x in rng.integers(0, 400, batch)]
+    lens[3] = lens[7] = lens[11] = 250                      # ties
+    q_lens = [1] * batch
+    for i in (5, batch - 2):                                # padding slots
+        q_lens[i], lens[i] = 0, 0
+    c = Case(name=f"decode_varlen_order_b{batch}", q_lens=q_lens, cache_seqlens=lens,
+             num_heads_q=8, num_heads_kv=2, head_dim=64, dtype="f16", page_size=16, append=True,
+             causal=True, seed=5200 + batch)
+    inp, _ = run_parity(c, splits=(1,))
+    # bit-exact against calls over a few single sequences
+    kc_after, vc_after = inp.k_cache.clone(), inp.v_cache.clone()
+    cu = inp.cu_seqlens_q.cpu().tolist()
+    seq_after = (inp.cache_seqlens + torch.tensor(q_lens, dtype=torch.int32, device="cuda")).contiguous()
+    full_out, full_lse = pa.paged_attn_fwd(inp.q, kc_after, vc_after, inp.block_table, seq_after,
+                                           inp.cu_seqlens_q, max_seqlen_q=1, causal=True, num_splits=1)
+    torch.cuda.synchronize()
+    for b in (0, 3, 7, int(np.argmax(lens)), batch - 1):
+        s_, e_ = cu[b], cu[b + 1]
+        if e_ == s_:
+            continue
+        o1, l1 = pa.paged_attn_fwd(
+            inp.q[s_:e_].contiguous(), kc_after, vc_after, inp.block_table[b:b + 1].contiguous(),
+            seq_after[b:b + 1].contiguous(), torch.tensor([0, 1], dtype=torch.int32, device="cuda"),
+            max_seqlen_q=1, causal=True, num_splits=1)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, full_out[s_:e_]) and torch.equal(l1, full_lse[s_:e_]), f"sequence {b}"
+
+
 def test_zero_length_padding_slots():
     c = wl.unified_varlen(50, heads=12, head_dim=64)
     c.q_lens = c.q_lens[:5]
