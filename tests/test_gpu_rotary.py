@@ -169,3 +169,55 @@ def test_rotary_append_only_entry_point_bit_exact(interleaved):
                                                    host(inp.cache_seqlens),
                                                    host(inp.cu_seqlens_q), host(inp.k_new),
                                                    host(inp.v_new))[0])
+
+
+def test_rotary_call_replays_from_a_graph():
+    # the fused rotary path under graph capture: one capture, replays with new
+    # queries and keys loaded into the same buffers equal eager calls bit for bit
+    c = wl.unified_varlen(60, heads=8, head_dim=128)
+    say(f"case {c.name} (graph)")
+    inp = make_inputs(c, "cuda")
+    cos, sin = wl.rotary_tables(max(c.keys_visible()) + 1, 128, c.dtype)
+    kc0, vc0 = inp.k_cache.clone(), inp.v_cache.clone()
+    out = torch.empty_like(inp.q)
+    lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def call():
+        pa.paged_attn_fwd(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens,
+                          inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q,
+                          max_seqlen_k=inp.max_seqlen_k, k_new=inp.k_new, v_new=inp.v_new,
+                          causal=True, out=out, softmax_lse=lse, rotary_cos=cos, rotary_sin=sin)
+
+    def load(seed):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        for t in (inp.q, inp.k_new, inp.v_new):
+            t.copy_(torch.rand(t.shape, generator=g, device="cuda").to(t.dtype))
+        inp.k_cache.copy_(kc0)
+        inp.v_cache.copy_(vc0)
+
+    eager = []
+    for seed in (11, 12):
+        load(seed)
+        call()
+        torch.cuda.synchronize()
+        eager.append((out.clone(), lse.clone(), inp.k_cache.clone()))
+    load(11)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, seed in enumerate((11, 12)):
+            load(seed)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager[i][0]) and torch.equal(lse, eager[i][1]), f"replay {rep}/{i}"
+            assert torch.equal(inp.k_cache, eager[i][2]), f"replay {rep}/{i}: rotated keys"
