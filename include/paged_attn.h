@@ -53,8 +53,10 @@ typedef enum pa_status {
                              2 GiB or more */
   PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than paged_attn_workspace_size */
   PA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
-  PA_ERR_ALIGN = 7        /* a buffer read or written in 16-byte vectors (q, caches,
+  PA_ERR_ALIGN = 7,       /* a buffer read or written in 16-byte vectors (q, caches,
                              k_new, v_new, out, rotary tables) is not 16-byte aligned */
+  PA_ERR_PRECONDITION = 8 /* device metadata breaks a precondition; only reported when
+                             the environment sets PAGED_ATTN_DEBUG=1 (see below) */
 } pa_status;
 
 typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
@@ -103,8 +105,15 @@ typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
  * Preconditions the host cannot check (device-resident metadata):
  *   q_len_b <= max_seqlen_q; K_b <= max_pages_per_seq * page_size (contiguous
  *   mode: K_b <= contig_alloc); the page ids read lie in [0, num_pages);
- *   append targets of different sequences are distinct slots; k_new/v_new do
- *   not alias the caches.  Device code never reads outside the table row or
+ *   append targets of different sequences are distinct slots.  (k_new/v_new
+ *   overlapping the caches is host-checkable: PA_ERR_SHAPE.)  With the
+ *   environment variable PAGED_ATTN_DEBUG=1, paged_attn_fwd and
+ *   paged_kv_append first synchronise the stream, copy cache_seqlens,
+ *   cu_seqlens_q and block_table to the host and check these (and that
+ *   cu_seqlens_q starts at 0, does not decrease and ends within total_q, and
+ *   K_b <= max_seqlen_k when given), returning PA_ERR_PRECONDITION before any
+ *   launch if one fails; that mode syncs, so such a call cannot be captured
+ *   in a graph.  Otherwise device code never reads outside the table row or
  *   the pool: a key whose page id is out of range is read as a zero K row and
  *   a zero V row (no error is raised; the result is then unspecified beyond
  *   being finite), and an append to such a slot is dropped.
@@ -144,6 +153,14 @@ typedef struct pa_fwd_args {
   int32_t rotary_interleaved;/* 0: pairs (j, j + rotary_dim / 2); 1: pairs (2j, 2j + 1) */
   int32_t rotary_rows;       /* with tables: rows (positions) they hold, >= 1; else 0 */
   int32_t reserved1;         /* must be 0 */
+  /* Row strides, in elements, between consecutive tokens of q, k_new and
+   * v_new (0: dense, num_heads * head_dim).  The heads and head_dim of a row
+   * stay dense; a stride lets the three be views into one fused QKV
+   * projection output.  A nonzero stride is at least the row size and a
+   * multiple of 8 (16-byte aligned rows). */
+  int64_t q_row_stride;
+  int64_t k_new_row_stride;
+  int64_t v_new_row_stride;
 } pa_fwd_args;
 
 /*

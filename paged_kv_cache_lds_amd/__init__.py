@@ -58,6 +58,8 @@ class _Args(ctypes.Structure):
         ("rotary_cos", ctypes.c_void_p), ("rotary_sin", ctypes.c_void_p),
         ("rotary_dim", ctypes.c_int32), ("rotary_interleaved", ctypes.c_int32),
         ("rotary_rows", ctypes.c_int32), ("reserved1", ctypes.c_int32),
+        ("q_row_stride", ctypes.c_int64), ("k_new_row_stride", ctypes.c_int64),
+        ("v_new_row_stride", ctypes.c_int64),
     ]
 
 
@@ -116,6 +118,23 @@ def _check_dev(name, t, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _check_rows(name, t, dtype):
+    """q / k_new / v_new: [tokens, heads, head_dim] with heads and head_dim dense;
+    the token stride may be larger (a view into a fused QKV output).  Returns
+    the row stride to pass (0 when dense)."""
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be [tokens, heads, head_dim] with heads and head_dim dense")
+    if t.is_contiguous():
+        return 0
+    return int(t.stride(0))
+
+
 def _set_rotary(a: _Args, rotary_cos, rotary_sin, rotary_interleaved, dtype) -> None:
     """Fill the rotary fields: tables [rows, rotary_dim / 2] in the element type."""
     if (rotary_cos is None) != (rotary_sin is None):
@@ -141,9 +160,11 @@ def make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *, 
     dt = q.dtype
     if dt not in _DTYPE_CODE:
         raise TypeError("q must be float16 or bfloat16")
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
-                    ("v_new", v_new), ("out", out)):
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
         _check_dev(name, t, dt)
+    q_stride = _check_rows("q", q, dt)
+    kn_stride = _check_rows("k_new", k_new, dt)
+    vn_stride = _check_rows("v_new", v_new, dt)
     for name, t in (("block_table", block_table), ("cache_seqlens", cache_seqlens),
                     ("cu_seqlens_q", cu_seqlens_q)):
         _check_dev(name, t, torch.int32)
@@ -182,6 +203,7 @@ def make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *, 
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _set_rotary(a, rotary_cos, rotary_sin, rotary_interleaved, dt)
+    a.q_row_stride, a.k_new_row_stride, a.v_new_row_stride = q_stride, kn_stride, vn_stride
     return a
 
 
@@ -242,9 +264,10 @@ def paged_kv_append(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, 
     """Write k_new/v_new rows at positions cache_seqlens[b] + i (bit copy; keys
     rotated at those positions first when rotary tables are given)."""
     dt = k_cache.dtype
-    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
-                    ("v_new", v_new)):
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
         _check_dev(name, t, dt)
+    kn_stride = _check_rows("k_new", k_new, dt)
+    vn_stride = _check_rows("v_new", v_new, dt)
     a = _Args()
     a.dtype = _DTYPE_CODE[dt]
     a.batch = cache_seqlens.shape[0]
@@ -266,6 +289,7 @@ def paged_kv_append(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, 
     a.cu_seqlens_q = _ptr(cu_seqlens_q)
     a.k_new = _ptr(k_new)
     a.v_new = _ptr(v_new)
+    a.k_new_row_stride, a.v_new_row_stride = kn_stride, vn_stride
     _set_rotary(a, rotary_cos, rotary_sin, rotary_interleaved, dt)
     st = _lib().paged_kv_append(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream)))
     if st != 0:

@@ -36,6 +36,7 @@ struct FwdParams {
   float scale_log2;    // softmax scale * log2(e)
   int all_decode;      // host knows every sequence has q_len * group <= 16
   Rotary rot;          // rotary embedding of q (rot.cos == nullptr: none)
+  long q_stride;       // elements between consecutive tokens' q rows
 };
 
 struct AppendParams {
@@ -48,6 +49,7 @@ struct AppendParams {
   const uint16_t *v_new;
   int batch, total_q, hkv, head_dim, tokens_per_block;
   Rotary rot;          // rotary embedding of the new keys (rot.cos == nullptr: none)
+  long kn_stride, vn_stride;   // elements between consecutive tokens' k_new / v_new rows
 };
 
 // ---------------------------------------------------------------------------
@@ -78,9 +80,9 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
     const int i = tok0 + t;
     const long prow = physical_row(p.geom, b, L + i);
     if (prow < 0) continue;
-    const long src = ((long)(cu_b + i) * vec_per_row + v) * 8;
     const long dst = (prow * vec_per_row + v) * 8;
     if (which == 0) {
+      const long src = (long)(cu_b + i) * p.kn_stride + v * 8;
       u32x4 k[1] = {load16(p.k_new + src)};
       if (p.rot.cos != nullptr) {
         const int e0 = (v % (p.head_dim >> 3)) * 8;   // offset inside the head row
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
       }
       store16(p.k_cache + dst, k[0]);
     } else {
-      store16(p.v_cache + dst, load16(p.v_new + src));
+      store16(p.v_cache + dst, load16(p.v_new + (long)(cu_b + i) * p.vn_stride + v * 8));
     }
   }
 }

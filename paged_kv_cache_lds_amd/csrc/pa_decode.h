@@ -73,7 +73,7 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
 
   u32x4 qf[DS];
   {
-    const uint16_t *qrow = p.q + ((long)(si.cu_b + tok) * p.hq + h) * D;
+    const uint16_t *qrow = p.q + (long)(si.cu_b + tok) * p.q_stride + (long)h * D;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
       qf[ds] = row_ok ? load16(qrow + (ds * 4 + lg) * 8) : u32x4{0u, 0u, 0u, 0u};
@@ -85,7 +85,8 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
   const int rot_pos = row_ok ? si.K_b - si.q_len + tok : -1;
   RotFetch<DS> rotf;
   if (rot_q)
-    rot_fetch(p.rot, p.q + ((long)(si.cu_b + tok) * p.hq + h) * D, lg * 8, 32, rot_pos, rotf);
+    rot_fetch(p.rot, p.q + (long)(si.cu_b + tok) * p.q_stride + (long)h * D, lg * 8, 32, rot_pos,
+              rotf);
 
   const CacheGeom &cg = p.geom;
   const bool paged = cg.table != nullptr;

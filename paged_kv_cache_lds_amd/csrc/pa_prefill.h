@@ -76,7 +76,7 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
 
   u32x4 qf[QS];
   {
-    const uint16_t *qrow = p.q + ((long)(si.cu_b + tok) * p.hq + hq) * D;
+    const uint16_t *qrow = p.q + (long)(si.cu_b + tok) * p.q_stride + (long)hq * D;
 #pragma unroll
     for (int ds = 0; ds < QS; ++ds)
       qf[ds] = row_ok ? load16(qrow + ds * 16 + 8 * hh) : u32x4{0u, 0u, 0u, 0u};

@@ -5,9 +5,13 @@
 // frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
 
 #include "paged_attn.h"
 #include "pa_kernels.h"
@@ -74,6 +78,14 @@ pa_status validate(const pa_fwd_args *a, bool append_only, bool sizes_only = fal
     if (a->rotary_rows < 1 || (a->rotary_interleaved != 0 && a->rotary_interleaved != 1))
       return PA_ERR_SHAPE;
   }
+  // row strides of q / k_new / v_new: 0 (dense) or >= the row, 16-byte aligned
+  const long qrow = (long)a->num_heads_q * a->head_dim, kvrow = (long)a->num_heads_kv * a->head_dim;
+  if (a->q_row_stride < 0 || a->k_new_row_stride < 0 || a->v_new_row_stride < 0) return PA_ERR_SHAPE;
+  if ((a->q_row_stride != 0 && (!append_only && a->q_row_stride < qrow)) ||
+      (a->k_new_row_stride != 0 && a->k_new_row_stride < kvrow) ||
+      (a->v_new_row_stride != 0 && a->v_new_row_stride < kvrow))
+    return PA_ERR_SHAPE;
+  if ((a->q_row_stride | a->k_new_row_stride | a->v_new_row_stride) % 8 != 0) return PA_ERR_ALIGN;
   if (!sizes_only) {
     // every buffer the kernels move in 16-byte vectors
     const void *vec[] = {a->k_cache, a->v_cache, a->k_new, a->v_new, a->rotary_cos,
@@ -81,6 +93,27 @@ pa_status validate(const pa_fwd_args *a, bool append_only, bool sizes_only = fal
                          append_only ? nullptr : a->out};
     for (const void *v : vec)
       if ((reinterpret_cast<uintptr_t>(v) & 15u) != 0) return PA_ERR_ALIGN;
+  }
+  if (!sizes_only && a->k_new != nullptr) {
+    // new rows must not overlap the pools they are appended to
+    const long rows = std::max(0, a->total_q);
+    const size_t pool_bytes =
+        (a->block_table != nullptr ? (size_t)a->num_pages * a->page_size
+                                   : (size_t)a->batch * a->contig_alloc) * (size_t)kvrow * 2;
+    auto span = [&](const void *p, long stride) {
+      const size_t n = rows == 0 ? 0
+                                 : ((size_t)(rows - 1) * (size_t)(stride ? stride : kvrow) +
+                                    (size_t)kvrow) * 2;
+      return std::pair<uintptr_t, uintptr_t>((uintptr_t)p, (uintptr_t)p + n);
+    };
+    auto overlap = [](std::pair<uintptr_t, uintptr_t> x, const void *pool, size_t bytes) {
+      const uintptr_t lo = (uintptr_t)pool, hi = lo + bytes;
+      return x.first < hi && lo < x.second;
+    };
+    const auto kn = span(a->k_new, a->k_new_row_stride), vn = span(a->v_new, a->v_new_row_stride);
+    if (overlap(kn, a->k_cache, pool_bytes) || overlap(kn, a->v_cache, pool_bytes) ||
+        overlap(vn, a->k_cache, pool_bytes) || overlap(vn, a->v_cache, pool_bytes))
+      return PA_ERR_SHAPE;
   }
   if (append_only) {
     if (a->k_new == nullptr) return PA_ERR_NULL;
@@ -154,6 +187,61 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
   return pl;
 }
 
+// PAGED_ATTN_DEBUG=1: read the device metadata back (synchronising the
+// stream) and check the preconditions the kernels rely on.
+bool debug_checks() {
+  const char *e = std::getenv("PAGED_ATTN_DEBUG");
+  return e != nullptr && std::strcmp(e, "1") == 0;
+}
+
+pa_status check_preconditions(const pa_fwd_args *a, bool append_only, hipStream_t stream) {
+  if (hipStreamSynchronize(stream) != hipSuccess) return PA_ERR_HIP;
+  const int B = a->batch;
+  std::vector<int32_t> seq(B), cu(B + 1);
+  if (hipMemcpy(seq.data(), a->cache_seqlens, sizeof(int32_t) * B, hipMemcpyDeviceToHost) !=
+          hipSuccess ||
+      hipMemcpy(cu.data(), a->cu_seqlens_q, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost) !=
+          hipSuccess)
+    return PA_ERR_HIP;
+  const bool paged = a->block_table != nullptr;
+  std::vector<int32_t> table;
+  if (paged) {
+    table.resize((size_t)B * a->max_pages_per_seq);
+    if (hipMemcpy(table.data(), a->block_table, sizeof(int32_t) * table.size(),
+                  hipMemcpyDeviceToHost) != hipSuccess)
+      return PA_ERR_HIP;
+  }
+  if (cu[0] != 0 || cu[B] > a->total_q) return PA_ERR_PRECONDITION;
+  const bool appends = a->k_new != nullptr;
+  const long cap = paged ? (long)a->max_pages_per_seq * a->page_size : (long)a->contig_alloc;
+  std::vector<long> targets;
+  for (int b = 0; b < B; ++b) {
+    const long n = (long)cu[b + 1] - cu[b];
+    if (n < 0 || n > a->max_seqlen_q || seq[b] < 0) return PA_ERR_PRECONDITION;
+    const long K = seq[b] + (appends ? n : 0);
+    if (K > cap) return PA_ERR_PRECONDITION;
+    if (!append_only && a->max_seqlen_k > 0 && K > a->max_seqlen_k) return PA_ERR_PRECONDITION;
+    if (paged) {
+      for (long j = 0; j < (K + a->page_size - 1) / a->page_size; ++j) {
+        const int32_t pg = table[(size_t)b * a->max_pages_per_seq + j];
+        if (pg < 0 || pg >= a->num_pages) return PA_ERR_PRECONDITION;
+      }
+    }
+    if (appends) {
+      for (long i = 0; i < n; ++i) {
+        const long pos = seq[b] + i;
+        targets.push_back(paged ? (long)table[(size_t)b * a->max_pages_per_seq + pos / a->page_size] *
+                                          a->page_size + pos % a->page_size
+                                : (long)b * a->contig_alloc + pos);
+      }
+    }
+  }
+  std::sort(targets.begin(), targets.end());
+  if (std::adjacent_find(targets.begin(), targets.end()) != targets.end())
+    return PA_ERR_PRECONDITION;
+  return PA_OK;
+}
+
 pa::Rotary rotary_of(const pa_fwd_args *a) {
   pa::Rotary r;
   r.cos = static_cast<const uint16_t *>(a->rotary_cos);
@@ -189,6 +277,9 @@ pa_status launch_append(const pa_fwd_args *a, hipStream_t stream) {
   p.hkv = a->num_heads_kv;
   p.head_dim = a->head_dim;
   p.rot = rotary_of(a);
+  const long kvrow = (long)a->num_heads_kv * a->head_dim;
+  p.kn_stride = a->k_new_row_stride ? a->k_new_row_stride : kvrow;
+  p.vn_stride = a->v_new_row_stride ? a->v_new_row_stride : kvrow;
   const int vec_per_row = a->num_heads_kv * a->head_dim / 8;
   p.tokens_per_block = std::max(1, 1024 / (2 * vec_per_row));
   dim3 grid((unsigned)cdiv(a->max_seqlen_q, p.tokens_per_block), (unsigned)a->batch);
@@ -205,6 +296,7 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   const int group = a->num_heads_q / a->num_heads_kv;
   pa::FwdParams p;
   p.q = static_cast<const uint16_t *>(a->q);
+  p.q_stride = a->q_row_stride ? a->q_row_stride : (long)a->num_heads_q * a->head_dim;
   p.k_cache = static_cast<const uint16_t *>(a->k_cache);
   p.v_cache = static_cast<const uint16_t *>(a->v_cache);
   p.geom = geom_of(a);
@@ -302,8 +394,12 @@ size_t paged_attn_workspace_size(const pa_fwd_args *args) {
 }
 
 pa_status paged_kv_append(const pa_fwd_args *args, void *stream) {
-  const pa_status st = validate(args, true);
+  pa_status st = validate(args, true);
   if (st != PA_OK) return st;
+  if (debug_checks()) {
+    st = check_preconditions(args, true, static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+  }
   return launch_append(args, static_cast<hipStream_t>(stream));
 }
 
@@ -311,6 +407,10 @@ pa_status paged_attn_fwd(const pa_fwd_args *args, void *stream) {
   pa_status st = validate(args, false);
   if (st != PA_OK) return st;
   if (args->total_q == 0) return PA_OK;
+  if (debug_checks()) {
+    st = check_preconditions(args, false, static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+  }
   const Plan pl = make_plan(args, device_cus());
   if (pl.ws_bytes > 0 && (args->workspace == nullptr || args->workspace_bytes < pl.ws_bytes))
     return PA_ERR_WORKSPACE;
@@ -337,6 +437,7 @@ const char *paged_attn_status_string(int32_t status) {
     case PA_ERR_WORKSPACE: return "workspace missing or smaller than paged_attn_workspace_size";
     case PA_ERR_HIP: return "a HIP launch or runtime call failed";
     case PA_ERR_ALIGN: return "a buffer moved in 16-byte vectors is not 16-byte aligned";
+    case PA_ERR_PRECONDITION: return "device metadata breaks a precondition (PAGED_ATTN_DEBUG=1)";
     default: return "unknown status";
   }
 }

@@ -94,6 +94,12 @@ def call_fwd(a):
     # 16-byte alignment of every buffer moved in 16-byte vectors
     (dict(q=0x1008), 7), (dict(out=0x1002), 7), (dict(k_cache=0x1004), 7),
     (dict(rotary_cos=0x3008, rotary_sin=0x4000, rotary_dim=32, rotary_rows=8), 7),
+    # row strides of q / k_new / v_new
+    (dict(q_row_stride=8), 2), (dict(q_row_stride=-256), 2), (dict(q_row_stride=4 * 64 + 4), 7),
+    (dict(k_new=0x100000, v_new=0x200000, k_new_row_stride=64), 2),
+    (dict(k_new=0x100000, v_new=0x200000, k_new_row_stride=4 * 64 + 8, v_new_row_stride=260), 7),
+    # new rows overlapping a pool they are appended to
+    (dict(k_new=0x1000, v_new=0x900000), 2), (dict(k_new=0x900000, v_new=0x1200), 2),
 ])
 def test_host_validation_codes(over, code):
     assert call_fwd(valid_args(**over)) == code
@@ -117,7 +123,7 @@ def test_workspace_size_and_splits_for_are_host_only():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         assert pa.paged_attn_status_string(code) != "unknown status"
     assert pa.paged_attn_status_string(99) == "unknown status"
 
