@@ -368,6 +368,8 @@ def main():
     ap.add_argument("--ctx", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the copy / GEMM ceiling measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--sweep", choices=["copy", "decode", "gqa", "prefill", "unified", "graph", "rotary",
@@ -477,7 +479,16 @@ def main():
         sub = wl.Case(**{**attn_case.__dict__, "q_lens": [1] * nseq,
                          "cache_seqlens": attn_case.cache_seqlens[:nseq]})
         cpu_gbs = algorithmic_bytes(sub) / tc / 1e9
+        cpu_model = ""
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         cpu = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model,
                "sample": f"{nseq} of {case.batch} sequences (all 32 heads, {args.ctx + 1} keys "
                          f"each) of the same decode step, fp64 gather-then-softmax, "
                          f"{tc:.2f} s"}
@@ -512,6 +523,29 @@ def main():
                    "peak": MFMA_F16_PEAK_TFS, "frac": round(tfs / MFMA_F16_PEAK_TFS, 4),
                    "flops_per_call": fl}
 
+    # ---- measured ceilings on this GPU: a streaming device copy (HBM) and a
+    # large fp16 GEMM through the vendor BLAS (MFMA), for the fractions of what
+    # the part reaches in practice beside the fractions of its peak ----
+    ceilings = None
+    if not args.no_ceilings:
+        torch.cuda.empty_cache()
+        n = 1 << 30                                   # 2 GiB of fp16 read + 2 GiB written
+        src = torch.empty(n, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        copy_ms = time_calls(lambda: dst.copy_(src), 10, 3, torch)
+        del src, dst
+        m = 8192
+        a_ = torch.rand(m, m, dtype=torch.float16, device="cuda")
+        b_ = torch.rand(m, m, dtype=torch.float16, device="cuda")
+        gemm_ms = time_calls(lambda: torch.matmul(a_, b_), 10, 3, torch)
+        del a_, b_
+        copy_gbs = 4.0 * n / (copy_ms * 1e-3) / 1e9
+        gemm_tfs = 2.0 * m ** 3 / (gemm_ms * 1e-3) / 1e12
+        ceilings = {"copy_GBps": round(copy_gbs, 1), "gemm_f16_TFLOPs": round(gemm_tfs, 1),
+                    "decode_frac_of_copy": round(achieved / copy_gbs, 4),
+                    "prefill_frac_of_gemm": (round(prefill["tflops"] / gemm_tfs, 4)
+                                             if prefill else None)}
+
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -521,7 +555,7 @@ def main():
                    "context": args.ctx, "heads_q": 32, "heads_kv": 32, "head_dim": 128,
                    "page_size": 16, "bytes_per_step": step_bytes, "splits": splits},
         "roofline": roofline, "cpu_baseline": cpu, "parity_sample": parity, "prefill": prefill,
-        "device": dev.name,
+        "ceilings": ceilings, "device": dev.name,
     }
     print(json.dumps(rec), flush=True)
 

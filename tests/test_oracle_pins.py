@@ -10,7 +10,8 @@ split merge) fails at least one of them:
   hand-derived worked examples in tests/golden/closed_forms.json;
 * invariants: physical page relabelling, page size (16...256 and contiguous),
   poisoned table tails, split-and-combine versus unsplit, causal decode versus
-  non-causal, GQA versus MHA with repeated kv heads, varlen versus one call per
+  non-causal, non-causal invariance under key order, GQA versus MHA with
+  repeated kv heads, varlen versus one call per
   sequence, (0, 0) padding slots;
 * append: bit-exact against a numpy fancy-index scatter, every other slot
   untouched;
@@ -356,6 +357,30 @@ def test_causal_decode_equals_noncausal():
         a = run_oracle(c, dtype="f16", causal=True)
         b = run_oracle(c, dtype="f16", causal=False)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_noncausal_result_ignores_key_order():
+    # without the causal mask attention is a function of the key set: shuffling
+    # the (K, V) rows within each sequence changes the fp64 result only by
+    # summation order
+    rng = np.random.default_rng(29)
+    c = random_case(rng, batch=3, q_lens=[2, 1, 3], cached=[50, 7, 130], hq=4, hkv=2, d=32, P=16,
+                    append=False, dtype="bf16", contiguous=True, dist="normal3")
+    a_out, a_lse, _, _ = run_oracle(c, dtype="bf16", causal=False)
+    kc, vc = c["kc"].copy(), c["vc"].copy()
+    for b, L in enumerate(c["seqlens"]):
+        perm = rng.permutation(int(L))
+        kc[b, :L] = c["kc"][b, perm]
+        vc[b, :L] = c["vc"][b, perm]
+    b_out, b_lse, _, _ = oracle.paged_attention(c["q"], kc, vc, None, c["seqlens"], c["cu"],
+                                                dtype="bf16", causal=False)
+    assert np.max(np.abs(a_out - b_out)) <= 1e-13 * max(1.0, np.abs(a_out).max())
+    assert np.max(np.abs(a_lse - b_lse)) <= 1e-13 * max(1.0, np.abs(a_lse).max())
+    # a causal call does depend on the order (a planted check that the shuffle bites)
+    c_out = oracle.paged_attention(c["q"], kc, vc, None, c["seqlens"], c["cu"], dtype="bf16",
+                                   causal=True)[0]
+    d_out = run_oracle(c, dtype="bf16", causal=True)[0]
+    assert np.max(np.abs(c_out - d_out)) > 1e-6
 
 
 def test_gqa_equals_mha_with_repeated_kv_heads():
