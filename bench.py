@@ -266,6 +266,10 @@ def sweep(name, reps, out_path):
                 c = wl.unified_varlen(nq, heads=heads, head_dim=hd)
                 inp = wl.make_inputs(c, "cuda")
                 S, med, mn = run(c, inp)
+                # the same call as one unified launch instead of two concurrent ones
+                os.environ["PAGED_ATTN_SINGLE_KERNEL"] = "1"
+                _, smed, _ = run(c, inp)
+                del os.environ["PAGED_ATTN_SINGLE_KERNEL"]
                 by, fl = algorithmic_bytes(c), causal_flops(c)
                 t_roof = max(by / (HBM_PEAK_GBS * 1e9), fl / (MFMA_F16_PEAK_TFS * 1e12)) * 1e3
                 # the same work as two calls: decode rows, then the prefill chunk
@@ -280,7 +284,7 @@ def sweep(name, reps, out_path):
                 dby = algorithmic_bytes(dec)
                 emit({"sweep": "unified", "nq": nq, "heads": heads, "head_dim": hd, "splits": S,
                       "ms": med, "ms_min": mn, "roofline_ms": t_roof, "frac": t_roof / med,
-                      "two_call_ms": dmed + pmed, "decode_only_ms": dmed,
+                      "one_launch_ms": smed, "two_call_ms": dmed + pmed, "decode_only_ms": dmed,
                       "decode_only_frac": dby / (HBM_PEAK_GBS * 1e9) * 1e3 / dmed})
                 del inp, di, pi
                 torch.cuda.empty_cache()

@@ -15,11 +15,13 @@
  * Conventions shared by every entry point
  *  - Pure C: no HIP or C++ types cross this boundary.  A stream is passed as
  *    `void *` holding a hipStream_t (NULL = the legacy default stream).
- *  - Every device buffer is owned by the caller.  The library never allocates,
- *    frees or synchronises inside paged_attn_fwd / paged_kv_append (the
- *    reproduction-script thread notes the call reaches memory only through the
- *    block table; the determine_num_splits issue rules out reading device
- *    lengths back to the host).  Scratch space comes in through `workspace`.
+ *  - Every device buffer is owned by the caller.  The library never allocates
+ *    device memory, frees or synchronises inside paged_attn_fwd /
+ *    paged_kv_append (the reproduction-script thread notes the call reaches
+ *    memory only through the block table; the determine_num_splits issue rules
+ *    out reading device lengths back to the host).  Scratch space comes in
+ *    through `workspace`; the only runtime objects the library creates are the
+ *    per-thread side stream and events described at paged_attn_fwd.
  *  - Launch shape and kernel choice depend only on host-side fields, so a call
  *    can be captured in a HIP graph; the CUDA-graph comment of the "Unify the
  *    kernel" thread sets the rule: static maxima, static metadata buffers,
@@ -167,9 +169,21 @@ typedef struct pa_fwd_args {
  * paged_attn_fwd - the whole forward call on `stream`: append k_new/v_new into
  * the pages (if given), attend over each sequence's cache, and - when the
  * split-KV count is above one - merge the per-split partial results with a
- * log-sum-exp combine.  Kernels run in that order on the one stream; the call
+ * log-sum-exp combine.  Kernels run in that order on `stream`; the call
  * returns as soon as they are queued.
- * Returns PA_OK or the first host-detected error (nothing launched then).
+ * A batch whose sizes allow both decode-mode sequences (q_len * group <= 16)
+ * and prefill-mode ones runs its attention as two concurrent launches: the
+ * decode units on a side stream that waits on `stream` (an event after the
+ * append), the prefill units on `stream`, which then waits on the side stream
+ * (a second event) before the combine.  Work queued on `stream` afterwards
+ * therefore sees the whole call, and a capture of `stream` takes in both
+ * launches.  The side stream and its two events are created on the first such
+ * call of a host thread on a device (default priority, non-blocking) and live
+ * as long as the thread; a first call made while `stream` is being captured,
+ * or any call with the environment variable PAGED_ATTN_SINGLE_KERNEL=1, runs
+ * the attention as one unified launch instead (same results, bit for bit).
+ * Returns PA_OK or the first host-detected error (nothing launched then);
+ * PA_ERR_HIP if a launch or an event operation fails.
  */
 pa_status paged_attn_fwd(const pa_fwd_args *args, void *stream);
 

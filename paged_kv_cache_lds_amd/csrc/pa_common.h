@@ -37,6 +37,8 @@ struct FwdParams {
   int all_decode;      // host knows every sequence has q_len * group <= 16
   Rotary rot;          // rotary embedding of q (rot.cos == nullptr: none)
   long q_stride;       // elements between consecutive tokens' q rows
+  int unit_mode;       // 0: every unit; 1: prefill units only; 2: decode units only
+                       // (a mixed batch split over two concurrent launches)
 };
 
 struct AppendParams {
@@ -48,6 +50,8 @@ struct AppendParams {
   const uint16_t *k_new;
   const uint16_t *v_new;
   int batch, total_q, hkv, head_dim, tokens_per_block;
+  int seq_mode, group; // 0: every sequence; 1: prefill-mode only; 2: decode-mode only
+                       // (q_len * group <= kDecodeRows)
   Rotary rot;          // rotary embedding of the new keys (rot.cos == nullptr: none)
   long kn_stride, vn_stride;   // elements between consecutive tokens' k_new / v_new rows
 };
@@ -68,6 +72,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
   const int q_len = max(0, min(p.cu_seqlens_q[b + 1], p.total_q) - cu_b);
   const int tok0 = blockIdx.x * p.tokens_per_block;
   if (tok0 >= q_len) return;
+  if (p.seq_mode != 0 && (p.seq_mode == 2) != (q_len * p.group <= kDecodeRows)) return;
   const int ntok = min(p.tokens_per_block, q_len - tok0);
   const int vec_per_row = p.hkv * p.head_dim / 8;   // 16-byte vectors per token row
   const int L = p.cache_seqlens[b];
@@ -268,9 +273,12 @@ __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool
   const int half = kDecPerWg == 2 ? tid / (NT / 2) : 0;
   const int S = p.num_splits;
   auto is_decode = [&](int rows) { return p.all_decode || rows <= kDecodeRows; };
-  // pass 1: prefill units, and (split budget) decode-mode sequences and their key tiles
+  // pass 1: prefill units, and (split budget) decode-mode sequences and their
+  // key tiles.  A prefill-only launch needs neither; a decode-only launch over
+  // a mixed batch needs the key tiles only.
   long extra = 0, total_tiles = 0, n_pre = 0;
-  if (S > 1 || !p.all_decode) {
+  const bool count_pre = !p.all_decode && p.unit_mode == 0;
+  if (p.unit_mode != 1 && (S > 1 || count_pre)) {
     long n_dec = 0, tiles = 0;
     for (int c0 = 0; c0 < p.batch; c0 += NT) {
       const int bb = c0 + tid;
@@ -292,7 +300,7 @@ __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool
         block_inclusive_scan<NT / 64>(dec, s_wsum, tot_d);
         block_inclusive_scan<NT / 64>(t, s_wsum, tot_t);
       }
-      if (!p.all_decode) block_inclusive_scan<NT / 64>(pre, s_wsum, tot_p);
+      if (count_pre) block_inclusive_scan<NT / 64>(pre, s_wsum, tot_p);
       n_dec += tot_d;
       tiles += tot_t;
       n_pre += tot_p;
@@ -300,9 +308,10 @@ __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool
     extra = n_dec * (S - 1);
     total_tiles = tiles;
   }
-  // pass 2: prefix over the units of our kind, find ours (one per half)
-  const bool pre_wg = wg < n_pre;
-  const long first = pre_wg ? wg : (wg - n_pre) * kDecPerWg;   // first unit index sought
+  // pass 2: prefix over the units of our kind, find ours (one per half).  A
+  // launch limited to one kind numbers its workgroups within that kind.
+  const bool pre_wg = p.unit_mode == 0 ? wg < n_pre : p.unit_mode == 1;
+  const long first = pre_wg ? wg : (p.unit_mode == 2 ? wg : wg - n_pre) * kDecPerWg;
   if (!pre_wg && p.batch <= kOrderMax && order != nullptr) {
     find_decode_ordered<NT, kDecPerWg>(p, first, extra, total_tiles, *order, s_wsum, s_found);
     const int slot = 3 * half;

@@ -28,12 +28,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   bool decode = true;
   bool have = true;
   if constexpr (!kUnified) {
-    // decode-only batches with one unit per sequence: units longest first (a
-    // varlen decode batch of 64 sequences x 32 heads ran 4% faster); past
-    // kOrderMax sequences, unit = sequence.  With a split budget the device
+    // decode units with one unit per sequence: longest first (a varlen decode
+    // batch of 64 sequences x 32 heads ran 4% faster); past kOrderMax
+    // sequences of an all-decode batch, unit = sequence.  With a split budget the device
     // share already evens the units out, and ordering would only add its
     // barriers.
-    if (p.num_splits == 1 && p.batch > kOrderMax) {
+    if (p.num_splits == 1 && p.batch > kOrderMax && p.unit_mode == 0) {
       u.b = wg;
       u.off = 0;
       u.splits = 1;
@@ -139,7 +139,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   }
 }
 
-// Decode-only batches (every sequence fits a decode unit, known on the host):
+// Decode-only batches (every sequence fits a decode unit, known on the host),
+// and the decode units of a mixed batch launched beside its prefill units:
 // four waves, two workgroups per CU.
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))

@@ -1,8 +1,9 @@
 // Host dispatch and C ABI of libpaged_attn.so (declarations and contracts in
 // include/paged_attn.h).  Validates arguments, plans the launch from
 // host-static sizes only, carves the caller's workspace and queues
-// append -> attention -> combine on the caller's stream.  Never allocates,
-// frees or synchronises.
+// append -> attention -> combine on the caller's stream (a mixed batch forks
+// its decode units onto a side stream and joins back before the combine).
+// Never allocates device memory, frees or synchronises.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -26,7 +27,10 @@ struct Plan {
   int splits = 1;         // split budget: average splits per decode sequence
   int max_splits = 1;     // most splits one sequence can receive
   bool all_decode = true;
-  long grid = 0;          // attention workgroups
+  bool may_mix = false;   // the batch can hold both decode-mode and prefill-mode sequences
+  long grid = 0;          // attention workgroups (one launch)
+  long grid_dec = 0;      // decode-only kernel over a mixed batch's decode units
+  long grid_pre = 0;      // unified kernel over its prefill units
   size_t ws_bytes = 0;
   size_t o_part_off = 0, lse_part_off = 0, count_off = 0;
   int max_seqlen_k = 0;
@@ -168,10 +172,17 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
   // cdiv(rows_b, kPrefillRows), at most cdiv(total rows, kPrefillRows) +
   // batch - 1.
   long units_per_head = (long)a->batch * pl.splits;
-  if (!pl.all_decode)
-    units_per_head = cdiv(units_per_head, 2) + cdiv((long)a->total_q * group, pa::kPrefillRows) +
-                     a->batch - 1;
+  const long pre_per_head = cdiv((long)a->total_q * group, pa::kPrefillRows) + a->batch - 1;
+  if (!pl.all_decode) units_per_head = cdiv(units_per_head, 2) + pre_per_head;
   pl.grid = units_per_head * a->num_heads_kv;
+  // A decode-mode sequence has 1 .. kDecodeRows / group new tokens.  The
+  // shortest sequence has at least total_q - (batch - 1) * max_seqlen_q; if
+  // that already exceeds a decode unit, every sequence is prefill-mode.
+  const long shortest = (long)a->total_q - (long)(a->batch - 1) * a->max_seqlen_q;
+  pl.may_mix = !pl.all_decode && group <= pa::kDecodeRows &&
+               std::max(1L, shortest) * group <= pa::kDecodeRows;
+  pl.grid_dec = (long)a->batch * pl.splits * a->num_heads_kv;
+  pl.grid_pre = pre_per_head * a->num_heads_kv;
   if (pl.splits > 1) {
     // the device shares the budget by sequence length (one split each, the
     // rest in proportion to key tiles): one sequence can get up to
@@ -242,6 +253,47 @@ pa_status check_preconditions(const pa_fwd_args *a, bool append_only, hipStream_
   return PA_OK;
 }
 
+// A mixed batch (decode-mode and prefill-mode sequences) runs as two
+// concurrent launches: the decode units in the decode-only kernel (four-wave
+// workgroups, two per CU, longest first) on a side stream, the prefill units in
+// the unified kernel on the caller's stream, joined by events.  Measured on
+// 64 decode sequences + one prefill chunk: 5-8% faster than one unified
+// launch at 32 heads x 128, equal at 12 x 64.  The side stream and the two
+// events are created once per host thread and device (default priority,
+// non-blocking) and kept for the thread's lifetime; a call made while the
+// caller's stream is being captured before they exist, or with
+// PAGED_ATTN_SINGLE_KERNEL=1, uses the one unified launch instead.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+
+SideStream *side_stream(hipStream_t caller) {
+  thread_local SideStream per_dev[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream &ss = per_dev[dev];
+  if (ss.s != nullptr) return &ss;
+  if (ss.failed) return nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return nullptr;
+  if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+    ss.failed = true;
+    ss.s = nullptr;
+    return nullptr;
+  }
+  return &ss;
+}
+
+bool single_kernel_forced() {
+  const char *e = std::getenv("PAGED_ATTN_SINGLE_KERNEL");
+  return e != nullptr && std::strcmp(e, "1") == 0;
+}
+
 pa::Rotary rotary_of(const pa_fwd_args *a) {
   pa::Rotary r;
   r.cos = static_cast<const uint16_t *>(a->rotary_cos);
@@ -262,7 +314,9 @@ pa::CacheGeom geom_of(const pa_fwd_args *a) {
   return g;
 }
 
-pa_status launch_append(const pa_fwd_args *a, hipStream_t stream) {
+// seq_mode: 0 every sequence, 1 prefill-mode sequences only, 2 decode-mode
+// sequences only (the two halves of a mixed batch's two launches)
+pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode = 0) {
   if (a->total_q == 0 || a->max_seqlen_q == 0) return PA_OK;
   pa::AppendParams p;
   p.k_cache = static_cast<uint16_t *>(a->k_cache);
@@ -282,7 +336,11 @@ pa_status launch_append(const pa_fwd_args *a, hipStream_t stream) {
   p.vn_stride = a->v_new_row_stride ? a->v_new_row_stride : kvrow;
   const int vec_per_row = a->num_heads_kv * a->head_dim / 8;
   p.tokens_per_block = std::max(1, 1024 / (2 * vec_per_row));
-  dim3 grid((unsigned)cdiv(a->max_seqlen_q, p.tokens_per_block), (unsigned)a->batch);
+  p.seq_mode = seq_mode;
+  p.group = a->num_heads_q / a->num_heads_kv;
+  const int rows = seq_mode == 2 ? std::min(a->max_seqlen_q, std::max(1, pa::kDecodeRows / p.group))
+                                 : a->max_seqlen_q;
+  dim3 grid((unsigned)cdiv(rows, p.tokens_per_block), (unsigned)a->batch);
   if (grid.y > 65535u) return PA_ERR_SHAPE;
   if (a->dtype == PA_BF16)
     hipLaunchKernelGGL(pa::kv_append_kernel<pa::kBF16>, grid, dim3(kThreads), 0, stream, p);
@@ -291,6 +349,7 @@ pa_status launch_append(const pa_fwd_args *a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+// append (if k_new) and attention; the combine follows on `stream`
 template <int DT, int D>
 pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t stream) {
   const int group = a->num_heads_q / a->num_heads_kv;
@@ -321,13 +380,41 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   p.scale_log2 = scale * pa::kLog2e;
   p.all_decode = pl.all_decode;
   p.rot = rotary_of(a);
-  if (pl.grid > 0x7fffffffL) return PA_ERR_SHAPE;
-  if (pl.all_decode)
+  p.unit_mode = 0;
+  if (pl.grid > 0x7fffffffL || pl.grid_dec > 0x7fffffffL || pl.grid_pre > 0x7fffffffL)
+    return PA_ERR_SHAPE;
+  SideStream *side = pl.may_mix && !single_kernel_forced() ? side_stream(stream) : nullptr;
+  const bool appends = a->k_new != nullptr;
+  if (side == nullptr && appends) {
+    const pa_status st = launch_append(a, stream);
+    if (st != PA_OK) return st;
+  }
+  if (pl.all_decode) {
     hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(kThreads),
                        0, stream, p);
-  else
+  } else if (side != nullptr) {
+    if (hipEventRecord(side->fork, stream) != hipSuccess ||
+        hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+      return PA_ERR_HIP;
+    // each launch appends the rows of its own sequences first
+    pa_status st = appends ? launch_append(a, side->s, 2) : PA_OK;
+    if (st != PA_OK) return st;
+    p.unit_mode = 2;
+    hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid_dec),
+                       dim3(kThreads), 0, side->s, p);
+    if (hipGetLastError() != hipSuccess || hipEventRecord(side->join, side->s) != hipSuccess)
+      return PA_ERR_HIP;
+    st = appends ? launch_append(a, stream, 1) : PA_OK;
+    if (st != PA_OK) return st;
+    p.unit_mode = 1;
+    hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid_pre),
+                       dim3(pa::kUThreads), 0, stream, p);
+    if (hipGetLastError() != hipSuccess || hipStreamWaitEvent(stream, side->join, 0) != hipSuccess)
+      return PA_ERR_HIP;
+  } else {
     hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(pa::kUThreads), 0,
                        stream, p);
+  }
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (pl.splits > 1) {
     pa::CombineParams c;
@@ -415,10 +502,6 @@ pa_status paged_attn_fwd(const pa_fwd_args *args, void *stream) {
   if (pl.ws_bytes > 0 && (args->workspace == nullptr || args->workspace_bytes < pl.ws_bytes))
     return PA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (args->k_new != nullptr) {
-    st = launch_append(args, s);
-    if (st != PA_OK) return st;
-  }
   const bool bf16 = args->dtype == PA_BF16;
   if (args->head_dim == 128)
     return bf16 ? launch_attention<pa::kBF16, 128>(args, pl, s)

@@ -223,6 +223,44 @@ def test_unified_varlen_with_prefix():
     run_parity(wl.unified_varlen(300, prefix=777))
 
 
+# A batch that can mix decode-mode and prefill-mode sequences runs as two
+# concurrent launches (decode units on a side stream); PAGED_ATTN_SINGLE_KERNEL=1
+# keeps the one unified launch.  Both plans run the same unit code, so they
+# must agree bit for bit, and the one-launch plan keeps its oracle parity.
+@pytest.mark.parametrize("nq,heads,hd", [(100, 32, 128), (1000, 12, 64)])
+def test_unified_varlen_one_launch(nq, heads, hd, monkeypatch):
+    monkeypatch.setenv("PAGED_ATTN_SINGLE_KERNEL", "1")
+    run_parity(wl.unified_varlen(nq, heads=heads, head_dim=hd), splits=(None, 2))
+
+
+@pytest.mark.parametrize("case", [wl.unified_varlen(300, prefix=777),
+                                  wl.unified_varlen(100, heads=12, head_dim=64),
+                                  wl.multi_token_decode(3, 700, 2)],
+                         ids=lambda c: c.name)
+def test_two_launches_equal_one_launch(case, monkeypatch):
+    if case.name.startswith("multi_token"):
+        # one prefill-mode sequence among decode-mode ones
+        case.q_lens = [2, 40, 2]
+    say(f"case {case.name} seed {case.seed}")
+    inp = make_inputs(case, "cuda")
+    kc0, vc0 = inp.k_cache.clone(), inp.v_cache.clone()
+    for s in (None, 2):
+        got = {}
+        for plan in ("two", "one"):
+            if plan == "one":
+                monkeypatch.setenv("PAGED_ATTN_SINGLE_KERNEL", "1")
+            else:
+                monkeypatch.delenv("PAGED_ATTN_SINGLE_KERNEL", raising=False)
+            inp.k_cache.copy_(kc0)
+            inp.v_cache.copy_(vc0)
+            out, lse = gpu_call(inp, num_splits=s)
+            got[plan] = (out.clone(), lse.clone(), inp.k_cache.clone(), inp.v_cache.clone())
+        for name, a, b in zip(("out", "lse", "k_cache", "v_cache"), got["two"], got["one"]):
+            bits = torch.int16 if a.element_size() == 2 else torch.int32
+            assert torch.equal(a.view(bits), b.view(bits)), \
+                f"{case.name} S={s}: {name} differs between the plans"
+
+
 # ---------------------------------------------------------------------------
 # Invariants that the kernels guarantee bit-exactly.
 # ---------------------------------------------------------------------------
