@@ -168,11 +168,14 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
                                           a->head_dim, a->max_seqlen_q, pl.max_seqlen_k, num_cus);
   // workgroups per kv head: one per decode unit (decode-only kernel); one per
   // prefill unit plus one per two decode units (unified kernel).  Decode
-  // units number at most batch * splits; prefill units, sum over sequences of
-  // cdiv(rows_b, kPrefillRows), at most cdiv(total rows, kPrefillRows) +
-  // batch - 1.
+  // units number at most batch * splits; prefill units, the sum over the n_p
+  // prefill-mode sequences of cdiv(rows_b, kPrefillRows), at most
+  // cdiv(total rows, kPrefillRows) + n_p - 1, where each such sequence has
+  // more than kDecodeRows rows.
   long units_per_head = (long)a->batch * pl.splits;
-  const long pre_per_head = cdiv((long)a->total_q * group, pa::kPrefillRows) + a->batch - 1;
+  const long total_rows = (long)a->total_q * group;
+  const long n_p = std::max(1L, std::min<long>(a->batch, total_rows / (pa::kDecodeRows + 1)));
+  const long pre_per_head = cdiv(total_rows, pa::kPrefillRows) + n_p - 1;
   if (!pl.all_decode) units_per_head = cdiv(units_per_head, 2) + pre_per_head;
   pl.grid = units_per_head * a->num_heads_kv;
   // A decode-mode sequence has 1 .. kDecodeRows / group new tokens.  The
