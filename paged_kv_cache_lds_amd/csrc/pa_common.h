@@ -178,6 +178,10 @@ struct DecodeOrder {
   int cnt[kOrderMax];   // by rank: its decode units (splits); 0 past the last rank
 };
 
+// ints per unit sought in the search's shared slots: sequence, split or
+// query tile, splits, and the sequence's cu_b, q_len, K_b
+constexpr int kFound = 6;
+
 // The decode unit(s) `first` .. `first + kDecPerWg - 1` (per kv head, in the
 // order above) into s_found, as in locate_unit's second pass.  Every thread of
 // the workgroup takes part; barriers are uniform.
@@ -206,7 +210,7 @@ __device__ inline void find_decode_ordered(const FwdParams &p, long first, long 
     my_key[i] = key;
     my_cnt[i] = cnt;
   }
-  if (tid < 3 * kDecPerWg) s_found[tid] = -1;
+  if (tid < kFound * kDecPerWg) s_found[tid] = -1;
   __syncthreads();
   bool unordered = false;
 #pragma unroll
@@ -241,14 +245,14 @@ __device__ inline void find_decode_ordered(const FwdParams &p, long first, long 
     for (int h = 0; h < kDecPerWg; ++h) {
       const long want = first + h;
       if (units > 0 && want >= excl && want < incl) {
-        s_found[3 * h] = o.seq[r];
-        s_found[3 * h + 1] = (int)(want - excl);
-        s_found[3 * h + 2] = units;
+        s_found[kFound * h] = o.seq[r];
+        s_found[kFound * h + 1] = (int)(want - excl);
+        s_found[kFound * h + 2] = units;
       }
     }
     carry += total;
     __syncthreads();
-    if (s_found[3 * (kDecPerWg - 1)] >= 0) break;   // the last one sought is found
+    if (s_found[kFound * (kDecPerWg - 1)] >= 0) break;   // the last one sought is found
   }
 }
 
@@ -264,6 +268,7 @@ __device__ inline void find_decode_ordered(const FwdParams &p, long first, long 
 // over the device metadata, and a workgroup or half without a unit returns.
 struct UnitInfo {
   int b, off, splits;   // off = split (decode) or query tile (prefill)
+  SeqInfo si;           // the sequence's metadata when the search read it (si.q_len < 0: not read)
 };
 
 template <int NT, int kDecPerWg>
@@ -314,21 +319,23 @@ __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool
   const long first = pre_wg ? wg : (p.unit_mode == 2 ? wg : wg - n_pre) * kDecPerWg;
   if (!pre_wg && p.batch <= kOrderMax && order != nullptr) {
     find_decode_ordered<NT, kDecPerWg>(p, first, extra, total_tiles, *order, s_wsum, s_found);
-    const int slot = 3 * half;
+    const int slot = kFound * half;
     u.b = s_found[slot];
     u.off = s_found[slot + 1];
     u.splits = s_found[slot + 2];
+    u.si.q_len = -1;
     decode = true;
     return u.b >= 0;
   }
-  if (tid < 6) s_found[tid] = -1;
+  if (tid < 2 * kFound) s_found[tid] = -1;
   __syncthreads();
   long carry = 0;
   for (int c0 = 0; c0 < p.batch; c0 += NT) {
     const int bb = c0 + tid;
     int units = 0, splits = 1;
+    SeqInfo si{0, 0, 0};
     if (bb < p.batch) {
-      const SeqInfo si = seq_info(p, bb);
+      si = seq_info(p, bb);
       const int rows = si.q_len * p.group;
       if (rows > 0) {
         if (is_decode(rows)) {
@@ -346,19 +353,27 @@ __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool
     for (int h = 0; h < n_sought; ++h) {
       const long want = first + h;
       if (units > 0 && want >= excl && want < incl) {
-        s_found[3 * h] = bb;
-        s_found[3 * h + 1] = (int)(want - excl);
-        s_found[3 * h + 2] = splits;
+        // the finder passes on what it read of the sequence, sparing the
+        // workgroup a dependent reload before the unit can start
+        s_found[kFound * h] = bb;
+        s_found[kFound * h + 1] = (int)(want - excl);
+        s_found[kFound * h + 2] = splits;
+        s_found[kFound * h + 3] = si.cu_b;
+        s_found[kFound * h + 4] = si.q_len;
+        s_found[kFound * h + 5] = si.K_b;
       }
     }
     carry += total;
     __syncthreads();
-    if (s_found[3 * (n_sought - 1)] >= 0) break;   // the last one sought is found
+    if (s_found[kFound * (n_sought - 1)] >= 0) break;   // the last one sought is found
   }
-  const int slot = pre_wg ? 0 : 3 * half;
+  const int slot = pre_wg ? 0 : kFound * half;
   u.b = s_found[slot];
   u.off = s_found[slot + 1];
   u.splits = s_found[slot + 2];
+  u.si.cu_b = s_found[slot + 3];
+  u.si.q_len = u.b >= 0 ? s_found[slot + 4] : -1;
+  u.si.K_b = s_found[slot + 5];
   decode = !pre_wg;
   return u.b >= 0;
 }

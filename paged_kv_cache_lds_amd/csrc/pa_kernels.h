@@ -20,7 +20,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   __shared__ float sm_m[NW][kDecodeRows];           // per-wave decode states (two halves
   __shared__ float sm_l[NW][kDecodeRows];           // of four in the unified kernel)
   __shared__ int s_wsum[NW];
-  __shared__ int s_found[6];
+  __shared__ int s_found[2 * kFound];
 
   const int g = blockIdx.x % p.hkv;
   const int wg = blockIdx.x / p.hkv;
@@ -37,6 +37,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
       u.b = wg;
       u.off = 0;
       u.splits = 1;
+      u.si.q_len = -1;
       have = u.b < p.batch;
     } else if (p.num_splits == 1) {
       __shared__ DecodeOrder s_order;
@@ -65,7 +66,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   u.b = __builtin_amdgcn_readfirstlane(u.b);
   u.off = __builtin_amdgcn_readfirstlane(u.off);
   u.splits = __builtin_amdgcn_readfirstlane(u.splits);
-  SeqInfo si = seq_info(p, u.b);
+  SeqInfo si = __builtin_amdgcn_readfirstlane(u.si.q_len) >= 0 ? u.si : seq_info(p, u.b);
   si.cu_b = __builtin_amdgcn_readfirstlane(si.cu_b);
   si.q_len = __builtin_amdgcn_readfirstlane(si.q_len);
   si.K_b = __builtin_amdgcn_readfirstlane(si.K_b);
