@@ -234,7 +234,11 @@ def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q
     ``max_seqlen_q`` must bound every q_len on the host side (no device read).
     ``rotary_cos`` / ``rotary_sin`` [rows, rotary_dim / 2] (element type) turn
     on the fused rotary embedding of q and k_new.
-    Returns (out [total_q, Hq, D], softmax_lse [total_q, Hq] fp32).
+    Everything is queued on ``stream`` (default: torch's current stream); a
+    batch that can mix decode-mode and prefill-mode sequences runs its decode
+    units on the library's side stream, forked from ``stream`` and joined back
+    into it before the call returns, so later work on ``stream`` sees the whole
+    result.  Returns (out [total_q, Hq, D], softmax_lse [total_q, Hq] fp32).
     """
     if out is None:
         out = torch.empty_like(q)
