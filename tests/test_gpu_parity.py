@@ -489,3 +489,31 @@ def test_every_tail_position_of_a_tile(P):
     c2 = Case(**{**c.__dict__, "name": f"tails_append_p{P}", "append": True, "causal": True,
                  "q_lens": [1, 2] * (n // 2), "head_dim": 64, "dtype": "bf16"})
     run_parity(c2, splits=(1, None))
+
+
+def test_mixed_batch_on_a_user_stream():
+    # a mixed batch queued on a stream of the caller's: work queued on that
+    # stream right after the call (no synchronisation) sees the whole result,
+    # which equals the same call on the default stream bit for bit
+    c = wl.unified_varlen(100, heads=8, head_dim=128)
+    say(f"case {c.name} seed {c.seed} on a user stream")
+    inp = make_inputs(c, "cuda")
+    kc0, vc0 = inp.k_cache.clone(), inp.v_cache.clone()
+    ref_out, ref_lse = gpu_call(inp)
+    ref_kc, ref_vc = inp.k_cache.clone(), inp.v_cache.clone()
+    inp.k_cache.copy_(kc0)
+    inp.v_cache.copy_(vc0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out, lse = pa.paged_attn_fwd(
+            inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens, inp.cu_seqlens_q,
+            max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=inp.max_seqlen_k, k_new=inp.k_new,
+            v_new=inp.v_new, causal=c.causal, stream=s)
+        out_copy, lse_copy = out.clone(), lse.clone()
+        kc_copy, vc_copy = inp.k_cache.clone(), inp.v_cache.clone()
+    torch.cuda.synchronize()
+    for name, a, b in (("out", out_copy, ref_out), ("lse", lse_copy, ref_lse),
+                       ("k_cache", kc_copy, ref_kc), ("v_cache", vc_copy, ref_vc)):
+        bits = torch.int16 if a.element_size() == 2 else torch.int32
+        assert torch.equal(a.view(bits), b.view(bits)), f"{name} differs on the user stream"
