@@ -260,7 +260,7 @@ pa_status check_preconditions(const pa_fwd_args *a, bool append_only, hipStream_
 // concurrent launches: the decode units in the decode-only kernel (four-wave
 // workgroups, two per CU, longest first) on a side stream, the prefill units in
 // the unified kernel on the caller's stream, joined by events.  Measured on
-// 64 decode sequences + one prefill chunk: 5-8% faster than one unified
+// 64 decode sequences + one prefill chunk: 3-7% faster than one unified
 // launch at 32 heads x 128, equal at 12 x 64.  The side stream and the two
 // events are created once per host thread and device (default priority,
 // non-blocking) and kept for the thread's lifetime; a call made while the
