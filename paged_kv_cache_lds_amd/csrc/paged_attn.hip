@@ -282,13 +282,21 @@ SideStream *side_stream(hipStream_t caller) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
     return nullptr;
-  if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
-      hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
+    // release whatever was created; the one-launch plan serves this thread
+    if (join != nullptr) (void)hipEventDestroy(join);
+    if (fork != nullptr) (void)hipEventDestroy(fork);
+    if (s != nullptr) (void)hipStreamDestroy(s);
     ss.failed = true;
-    ss.s = nullptr;
     return nullptr;
   }
+  ss.s = s;
+  ss.fork = fork;
+  ss.join = join;
   return &ss;
 }
 
