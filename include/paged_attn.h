@@ -201,7 +201,10 @@ pa_status paged_kv_append(const pa_fwd_args *args, void *stream);
 
 /*
  * paged_attn_workspace_size - bytes of device workspace paged_attn_fwd needs
- * for these arguments (0 when no split-KV partials are kept).  Host only; no
+ * for these arguments (0 when no split-KV partials are kept).  Basis: the
+ * small-page-size thread notes the paged call allocates nothing itself, so
+ * the split-KV partials of the determine_num_splits issue's split path live
+ * in caller-owned memory sized by this query.  Host only; no
  * device access.  Only sizes and flags are read (data pointers may still be
  * NULL; k_new/v_new only matter through being NULL or not).  Returns 0 for
  * invalid sizes as well.
@@ -228,7 +231,11 @@ int32_t paged_attn_num_splits(int32_t batch, int32_t total_q, int32_t num_heads_
                               int32_t max_seqlen_q, int32_t max_seqlen_k,
                               int32_t num_cus);
 
-/* paged_attn_status_string - static, human-readable text for a status code. */
+/* paged_attn_status_string - static, human-readable text for a status code.
+ * Basis: the pages report failures only as asynchronous CUDA errors far from
+ * their cause (the small-page-size thread's illegal-memory-access trace);
+ * here every host-detectable error is a status returned before any launch,
+ * and this names it. */
 const char *paged_attn_status_string(int32_t status);
 
 #ifdef __cplusplus

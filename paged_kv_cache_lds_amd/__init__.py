@@ -73,8 +73,14 @@ def library_path() -> str:
 def _lib():
     global _lib_handle
     if _lib_handle is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
+        if not _build.lib_is_current():
+            # missing, or built from other sources: rebuild, and fail loudly
+            # where no compiler is available rather than run a stale binary
+            try:
+                _build.build()
+            except Exception as e:
+                raise RuntimeError(f"{_build.LIB} is missing or older than its sources, and "
+                                   f"rebuilding it failed: {e}") from e
         lib = ctypes.CDLL(_build.LIB)
         P = ctypes.POINTER(_Args)
         lib.paged_attn_fwd.restype = ctypes.c_int
@@ -135,6 +141,51 @@ def _check_rows(name, t, dtype):
     return int(t.stride(0))
 
 
+def _shape(name, t, want):
+    """Raise unless tensor `t` has shape `want` (a tuple; None entries match anything)."""
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        raise ValueError(f"{name} has shape {list(got)}, expected "
+                         f"{['*' if w is None else w for w in want]}")
+
+
+def _check_same_gpu(**tensors):
+    """Every given tensor lives on one GPU (the kernels dereference them all
+    there): a host tensor or one on another device would be read through a
+    wrong address."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
+def _check_cache(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, head_dim):
+    """Shapes shared by the forward call and the append: pools, table, metadata.
+    Returns (batch, num_heads_kv)."""
+    if cache_seqlens.dim() != 1 or cache_seqlens.shape[0] < 1:
+        raise ValueError("cache_seqlens must be [batch] with batch >= 1")
+    batch = cache_seqlens.shape[0]
+    _shape("cu_seqlens_q", cu_seqlens_q, (batch + 1,))
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [num_pages, page_size, num_heads_kv, head_dim] "
+                         "(or [batch, alloc, num_heads_kv, head_dim] without a block table)")
+    _shape("v_cache", v_cache, tuple(k_cache.shape))
+    if k_cache.shape[3] != head_dim:
+        raise ValueError(f"k_cache head_dim {k_cache.shape[3]} != {head_dim}")
+    if block_table is not None:
+        _shape("block_table", block_table, (batch, None))
+    elif k_cache.shape[0] != batch:
+        raise ValueError("contiguous k_cache / v_cache must be [batch, alloc, num_heads_kv, "
+                         f"head_dim]: leading size {k_cache.shape[0]} != batch {batch}")
+    return batch, k_cache.shape[2]
+
+
 def _set_rotary(a: _Args, rotary_cos, rotary_sin, rotary_interleaved, dtype) -> None:
     """Fill the rotary fields: tables [rows, rotary_dim / 2] in the element type."""
     if (rotary_cos is None) != (rotary_sin is None):
@@ -156,7 +207,11 @@ def make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *, 
               max_seqlen_k=0, k_new=None, v_new=None, causal=False, num_splits=0,
               softmax_scale=None, out=None, softmax_lse=None, workspace=None, rotary_cos=None,
               rotary_sin=None, rotary_interleaved=False) -> _Args:
-    """Fill a ``pa_fwd_args`` from tensors (shapes read from the tensors)."""
+    """Fill a ``pa_fwd_args`` from tensors (shapes read from the tensors).
+
+    Every shape the kernels rely on is checked here, then that every tensor
+    is on one GPU; a mismatch raises before anything reaches the library.
+    ``out`` / ``softmax_lse`` may be None only for sizing queries."""
     dt = q.dtype
     if dt not in _DTYPE_CODE:
         raise TypeError("q must be float16 or bfloat16")
@@ -169,15 +224,30 @@ def make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *, 
                     ("cu_seqlens_q", cu_seqlens_q)):
         _check_dev(name, t, torch.int32)
     _check_dev("softmax_lse", softmax_lse, torch.float32)
+    _check_dev("workspace", workspace)
     total_q, hq, d = q.shape
+    batch, hkv = _check_cache(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, d)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        _shape("k_new", k_new, (total_q, hkv, d))
+        _shape("v_new", v_new, (total_q, hkv, d))
+    if out is not None:
+        _shape("out", out, (total_q, hq, d))
+    if softmax_lse is not None:
+        _shape("softmax_lse", softmax_lse, (total_q, hq))
+    _check_same_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                    cache_seqlens=cache_seqlens, cu_seqlens_q=cu_seqlens_q, k_new=k_new,
+                    v_new=v_new, out=out, softmax_lse=softmax_lse, workspace=workspace,
+                    rotary_cos=rotary_cos, rotary_sin=rotary_sin)
     a = _Args()
     a.dtype = _DTYPE_CODE[dt]
-    a.batch = cache_seqlens.shape[0]
+    a.batch = batch
     a.total_q = total_q
     a.max_seqlen_q = int(max_seqlen_q)
     a.max_seqlen_k = int(max_seqlen_k)
     a.num_heads_q = hq
-    a.num_heads_kv = k_cache.shape[2]
+    a.num_heads_kv = hkv
     a.head_dim = d
     if block_table is not None:
         a.page_size = k_cache.shape[1]
@@ -238,25 +308,33 @@ def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q
     batch that can mix decode-mode and prefill-mode sequences runs its decode
     units on the library's side stream, forked from ``stream`` and joined back
     into it before the call returns, so later work on ``stream`` sees the whole
-    result.  Returns (out [total_q, Hq, D], softmax_lse [total_q, Hq] fp32).
+    result.  Tensors the call allocates (out, softmax_lse, workspace when not
+    given) are allocated on ``stream``, so the caching allocator does not hand
+    them out again before the kernels queued there have finished.
+    Returns (out [total_q, Hq, D], softmax_lse [total_q, Hq] fp32).
     """
-    if out is None:
-        out = torch.empty_like(q)
-    if softmax_lse is None:
-        softmax_lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    # every check first: nothing is allocated or launched for bad arguments
     args = make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q,
                      max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, k_new=k_new,
                      v_new=v_new, causal=causal, num_splits=num_splits,
                      softmax_scale=softmax_scale, out=out, softmax_lse=softmax_lse,
                      workspace=workspace, rotary_cos=rotary_cos, rotary_sin=rotary_sin,
                      rotary_interleaved=rotary_interleaved)
-    if workspace is None:
-        need = paged_attn_workspace_size(args)
-        if need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            args.workspace = workspace.data_ptr()
-            args.workspace_bytes = need
-    st = _lib().paged_attn_fwd(ctypes.byref(args), ctypes.c_void_p(_stream_handle(stream)))
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty_like(q, memory_format=torch.contiguous_format)
+            args.out = out.data_ptr()
+        if softmax_lse is None:
+            softmax_lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+            args.softmax_lse = softmax_lse.data_ptr()
+        if workspace is None:
+            need = paged_attn_workspace_size(args)
+            if need > 0:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+                args.workspace = workspace.data_ptr()
+                args.workspace_bytes = need
+    st = _lib().paged_attn_fwd(ctypes.byref(args), ctypes.c_void_p(s.cuda_stream))
     if st != 0:
         raise PagedAttnError(st, "paged_attn_fwd")
     return out, softmax_lse
@@ -268,18 +346,32 @@ def paged_kv_append(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, 
     """Write k_new/v_new rows at positions cache_seqlens[b] + i (bit copy; keys
     rotated at those positions first when rotary tables are given)."""
     dt = k_cache.dtype
+    if dt not in _DTYPE_CODE:
+        raise TypeError("k_cache must be float16 or bfloat16")
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
         _check_dev(name, t, dt)
+    for name, t in (("block_table", block_table), ("cache_seqlens", cache_seqlens),
+                    ("cu_seqlens_q", cu_seqlens_q)):
+        _check_dev(name, t, torch.int32)
+    if k_new is None or v_new is None:
+        raise ValueError("paged_kv_append needs k_new and v_new")
     kn_stride = _check_rows("k_new", k_new, dt)
     vn_stride = _check_rows("v_new", v_new, dt)
+    d = k_new.shape[2]
+    batch, hkv = _check_cache(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, d)
+    _shape("k_new", k_new, (k_new.shape[0], hkv, d))
+    _shape("v_new", v_new, tuple(k_new.shape))
+    _check_same_gpu(k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                    cache_seqlens=cache_seqlens, cu_seqlens_q=cu_seqlens_q, k_new=k_new,
+                    v_new=v_new, rotary_cos=rotary_cos, rotary_sin=rotary_sin)
     a = _Args()
     a.dtype = _DTYPE_CODE[dt]
-    a.batch = cache_seqlens.shape[0]
+    a.batch = batch
     a.total_q = k_new.shape[0]
     a.max_seqlen_q = int(max_seqlen_q)
-    a.num_heads_q = k_new.shape[1]
-    a.num_heads_kv = k_new.shape[1]
-    a.head_dim = k_new.shape[2]
+    a.num_heads_q = hkv
+    a.num_heads_kv = hkv
+    a.head_dim = d
     if block_table is not None:
         a.page_size = k_cache.shape[1]
         a.num_pages = k_cache.shape[0]

@@ -1,6 +1,7 @@
 """Build libpaged_attn.so in-tree with hipcc for gfx950."""
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -10,6 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpaged_attn.so")
+# sha256 of the sources and flags the library was built from, written beside it
+STAMP = LIB + ".srchash"
 SOURCES = [os.path.join(CSRC, "paged_attn.hip")]
 ARCH = "gfx950"
 
@@ -30,6 +33,21 @@ def compile_flags():
     ]
 
 
+def source_hash(extra=()) -> str:
+    """sha256 over every source, header and compile flag the library is built
+    from (file contents, not modification times, so a copied tree keeps it)."""
+    h = hashlib.sha256()
+    deps = sorted(set(SOURCES + [os.path.join(CSRC, f) for f in os.listdir(CSRC)] +
+                      [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]))
+    for d in deps:
+        if os.path.isfile(d):
+            h.update(os.path.relpath(d, ROOT).encode())
+            with open(d, "rb") as fh:
+                h.update(fh.read())
+    h.update(" ".join(compile_flags() + list(extra)).encode())
+    return h.hexdigest()
+
+
 def build(out: str = LIB, extra=()) -> str:
     """Compile every HIP source of the library (always recompiles)."""
     tmp = out + ".tmp%d" % os.getpid()
@@ -38,16 +56,19 @@ def build(out: str = LIB, extra=()) -> str:
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
     os.replace(tmp, out)
+    if out == LIB and not extra:
+        with open(STAMP + ".tmp%d" % os.getpid(), "w") as fh:
+            fh.write(source_hash() + "\n")
+        os.replace(STAMP + ".tmp%d" % os.getpid(), STAMP)
     return out
 
 
-def sources_newer_than_lib() -> bool:
-    if not os.path.exists(LIB):
-        return True
-    t = os.path.getmtime(LIB)
-    deps = SOURCES + [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [
-        os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
-    return any(os.path.getmtime(d) > t for d in deps)
+def lib_is_current() -> bool:
+    """True when the built library exists and was built from the current sources."""
+    if not os.path.exists(LIB) or not os.path.exists(STAMP):
+        return False
+    with open(STAMP) as fh:
+        return fh.read().strip() == source_hash()
 
 
 if __name__ == "__main__":

@@ -1,6 +1,8 @@
 // Prefill unit of the gfx950 paged KV-cache attention forward pass.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_common.h"
 
 namespace pa {
@@ -357,8 +359,14 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   };
   // What a wave carries from one tile to the next, in sixteen integer
   // registers: group A the packed probabilities of its next tile, group B the
-  // bits of the scores of its next tile.
-  typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+  // bits of the scores of its next tile.  The carry must stay an integer
+  // vector: the same bits carried inside a float vector (bit-cast in and out)
+  // gave wrong outputs for group A's rows with the ROCm 7.2 compiler, while
+  // the integer carry is bit-exact; the assertions below keep it that way.
+  typedef uint32_t carry_word;
+  typedef carry_word u32x16 __attribute__((ext_vector_type(16)));
+  static_assert(std::is_integral<carry_word>::value && sizeof(u32x16) == 64,
+                "the ping-pong carry is sixteen integer words");
   auto put_p = [](const Probs &pr) -> u32x16 {
     u32x16 c;
 #pragma unroll
@@ -370,6 +378,8 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     }
     return c;
   };
+  static_assert(std::is_same<decltype(put_p(Probs{})), u32x16>::value,
+                "probabilities are carried in the integer vector");
   auto get_p = [](const u32x16 &c) -> Probs {
     Probs pr;
 #pragma unroll

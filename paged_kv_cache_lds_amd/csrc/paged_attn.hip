@@ -50,6 +50,8 @@ pa_status validate(const pa_fwd_args *a, bool append_only, bool sizes_only = fal
   if (a->reserved0 != 0) return PA_ERR_SHAPE;
   if (a->batch < 1 || a->total_q < 0 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0)
     return PA_ERR_SHAPE;
+  // the append grid holds one row of blocks per sequence (grid.y <= 65535)
+  if (a->k_new != nullptr && a->batch > 65535) return PA_ERR_SHAPE;
   if (a->total_q > 0 && a->max_seqlen_q < 1) return PA_ERR_SHAPE;
   if (a->num_heads_kv < 1) return PA_ERR_SHAPE;
   if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;

@@ -153,6 +153,103 @@ def test_causal_prefill_4x170():
     run_fullsize(c, {1: [0, 100, 169]})
 
 
+@pytest.mark.parametrize("prefix", ["zero", "uniform"])
+def test_causal_prefill_4x8192(prefix):
+    # the "and beyond" prefill size the prefill sweep times: early, middle and
+    # late rows, and both sides of two 256-row unit boundaries in sequence 0
+    c = wl.causal_prefill_append(8192, prefix)
+    run_fullsize(c, {0: [0, 255, 256, 4095, 4096, 8191], 2: [5000], 3: [31, 8190]})
+
+
+def sharp(c, seed_offset=77):
+    """The same shapes with q and keys ~ 3 N(0, 1): scores spread over tens of
+    units, so the softmax is dominated by a few keys and every rescaling path
+    of the kernels (running maximum, reference moves, bounded sums) is taken."""
+    return wl.Case(**{**c.__dict__, "values": "normal3", "seed": c.seed + seed_offset,
+                      "name": c.name + "_normal3"})
+
+
+@pytest.mark.parametrize("nq,prefix", [(2048, "zero"), (2048, "uniform"), (8192, "zero")])
+def test_causal_prefill_sharp_softmax_full_size(nq, prefix):
+    c = sharp(wl.causal_prefill_append(nq, prefix))
+    last = nq - 1
+    run_fullsize(c, {0: [0, 1, 300, nq // 2, last], 1: [last - 1], 3: [257, last]})
+
+
+@pytest.mark.parametrize("paged", [True, False])
+def test_gqa_long_split_sharp_softmax_full_size(paged):
+    c = sharp(wl.gqa_long_split(paged=paged))
+    run_fullsize(c, {b: [0] for b in range(c.batch)})
+
+
+def run_every_sequence(case, chunk=16):
+    """One whole GPU call, then EVERY sequence's rows against the oracle, in
+    chunks: the pools are copied on the GPU before the call; per chunk the
+    sequences' pages are gathered from that copy into a compact pool with a
+    fresh table, and the oracle appends and attends on it by itself."""
+    say(f"case {case.name} seed {case.seed} (full size, every sequence)")
+    inp = make_inputs(case, "cuda")
+    k0, v0 = inp.k_cache.clone(), inp.v_cache.clone()
+    cu = host(inp.cu_seqlens_q)
+    say("  gpu call")
+    out, lse = pa.paged_attn_fwd(
+        inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens, inp.cu_seqlens_q,
+        max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=inp.max_seqlen_k, k_new=inp.k_new,
+        v_new=inp.v_new, causal=case.causal)
+    torch.cuda.synchronize()
+    P = case.page_size
+    worst = 0.0
+    for c0 in range(0, case.batch, chunk):
+        bs = list(range(c0, min(case.batch, c0 + chunk)))
+        pages = [np.asarray(inp.pages_of[b], np.int64) for b in bs]
+        idx = torch.from_numpy(np.concatenate(pages)).to("cuda")
+        kc, vc = host(k0.index_select(0, idx)), host(v0.index_select(0, idx))
+        width = max(len(p) for p in pages)
+        table = np.full((len(bs), width), -1, np.int32)
+        off = 0
+        for i, p in enumerate(pages):
+            table[i, :len(p)] = np.arange(off, off + len(p))
+            off += len(p)
+        r0, r1 = int(cu[bs[0]]), int(cu[bs[-1] + 1])
+        cu_c = (cu[bs[0]:bs[-1] + 2] - cu[bs[0]]).astype(np.int32)
+        seq = np.asarray([case.cache_seqlens[b] for b in bs], np.int32)
+        kn = host(inp.k_new[r0:r1]) if case.append else None
+        vn = host(inp.v_new[r0:r1]) if case.append else None
+        ref_o, ref_l, ref_kc, ref_vc = oracle.paged_attention(
+            host(inp.q[r0:r1]), kc, vc, table, seq, cu_c, kn, vn, dtype=case.dtype,
+            causal=case.causal)
+        o = out[r0:r1].float().cpu().numpy().astype(np.float64)
+        l = lse[r0:r1].cpu().numpy().astype(np.float64)
+        err = np.abs(o - ref_o).max()
+        worst = max(worst, err)
+        assert err <= OUT_TOL, f"sequences {bs[0]}..{bs[-1]}: out err {err}"
+        fin = ~np.isneginf(ref_l)
+        assert np.array_equal(np.isneginf(l), ~fin), f"sequences {bs[0]}..{bs[-1]}: -inf pattern"
+        assert (np.abs(l[fin] - ref_l[fin]) <= LSE_REL * np.abs(ref_l[fin]) + LSE_ABS).all(), \
+            f"sequences {bs[0]}..{bs[-1]}: lse"
+        if case.append:
+            # the pages after the call hold what the oracle's own append wrote
+            kg = host(inp.k_cache.index_select(0, idx))
+            vg = host(inp.v_cache.index_select(0, idx))
+            for i, b in enumerate(bs):
+                rows = np.arange(table[i, 0] * P, table[i, 0] * P + len(pages[i]) * P)
+                K_b = case.cache_seqlens[b] + case.q_lens[b]
+                a = kg.reshape((-1,) + kg.shape[2:])[rows[:K_b]]
+                e = ref_kc.reshape((-1,) + ref_kc.shape[2:])[rows[:K_b]]
+                assert np.array_equal(a, e), f"sequence {b}: K pages after the call"
+                a = vg.reshape((-1,) + vg.shape[2:])[rows[:K_b]]
+                e = ref_vc.reshape((-1,) + ref_vc.shape[2:])[rows[:K_b]]
+                assert np.array_equal(a, e), f"sequence {b}: V pages after the call"
+    say(f"  {case.batch} sequences, max out err {worst:.3g}")
+    del inp, k0, v0
+    torch.cuda.empty_cache()
+
+
+def test_mha_decode_b256_ctx4096_every_sequence():
+    # the bench step (append one token, heuristic budget), all 256 x 32 rows
+    run_every_sequence(wl.mha_decode(256, 4096, append=True))
+
+
 @pytest.mark.parametrize("nq,heads,hd", [(100, 32, 128), (500, 32, 128), (1000, 32, 128),
                                          (100, 12, 64), (1000, 12, 64)])
 def test_unified_varlen_full(nq, heads, hd):

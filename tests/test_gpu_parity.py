@@ -517,3 +517,40 @@ def test_mixed_batch_on_a_user_stream():
                        ("k_cache", kc_copy, ref_kc), ("v_cache", vc_copy, ref_vc)):
         bits = torch.int16 if a.element_size() == 2 else torch.int32
         assert torch.equal(a.view(bits), b.view(bits)), f"{name} differs on the user stream"
+
+
+def test_allocations_follow_the_call_stream():
+    # stream= given without entering torch.cuda.stream(): the binding allocates
+    # out, softmax_lse and the split workspace on that stream, so allocations
+    # made on the current stream right after the call (filled while the call
+    # may still run) cannot take their blocks.  The result equals the same call
+    # on the current stream bit for bit.
+    c = wl.Case(name="gqa_split_stream", q_lens=[1] * 8, cache_seqlens=[4096 + 37 * i for i in range(8)],
+                num_heads_q=32, num_heads_kv=4, head_dim=128, dtype="bf16", page_size=16,
+                causal=True, num_splits=16, seed=7101)
+    say(f"case {c.name} seed {c.seed}: library allocations on a user stream")
+    inp = make_inputs(c, "cuda")
+    ref_out, ref_lse = gpu_call(inp)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    out, lse = pa.paged_attn_fwd(
+        inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens, inp.cu_seqlens_q,
+        max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=inp.max_seqlen_k, causal=c.causal,
+        num_splits=c.num_splits, stream=s)
+    # churn the current stream's pool with blocks of the workspace's size
+    args = pa.make_args(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens,
+                        inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q, causal=c.causal,
+                        num_splits=c.num_splits)
+    need = pa.paged_attn_workspace_size(args)
+    assert need > 0
+    junk = []
+    for _ in range(4):
+        j = torch.empty(need, dtype=torch.uint8, device="cuda")
+        j.fill_(0xFF)
+        junk.append(j)
+        o2 = torch.empty_like(inp.q)
+        o2.fill_(float("nan"))
+        junk.append(o2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "out differs"
+    assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), "lse differs"
