@@ -75,6 +75,8 @@ def target_rows(inp):
     cu = host(inp.cu_seqlens_q)
     table = host(inp.block_table)
     rows, toks = [], []
+    if not c.append:
+        return np.asarray(rows, np.int64), np.asarray(toks, np.int64)
     for b in range(c.batch):
         L = c.cache_seqlens[b]
         for i in range(int(cu[b + 1] - cu[b])):
