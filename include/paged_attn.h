@@ -21,7 +21,8 @@
  *    memory only through the block table; the determine_num_splits issue rules
  *    out reading device lengths back to the host).  Scratch space comes in
  *    through `workspace`; the only runtime objects the library creates are the
- *    per-thread side stream and events described at paged_attn_fwd.
+ *    two events of a forked call described at paged_attn_fwd, released by
+ *    the call.
  *  - Launch shape and kernel choice depend only on host-side fields, so a call
  *    can be captured in a HIP graph; the CUDA-graph comment of the "Unify the
  *    kernel" thread sets the rule: static maxima, static metadata buffers,
@@ -163,25 +164,32 @@ typedef struct pa_fwd_args {
   int64_t q_row_stride;
   int64_t k_new_row_stride;
   int64_t v_new_row_stride;
+  /* Optional second stream (hipStream_t; NULL: none) for a batch that mixes
+   * decode-mode and prefill-mode sequences: its decode units then run on it,
+   * concurrently with the prefill units on the call's stream (see
+   * paged_attn_fwd).  Owned by the caller; the library only queues work on it. */
+  void *aux_stream;
 } pa_fwd_args;
 
 /*
  * paged_attn_fwd - the whole forward call on `stream`: append k_new/v_new into
- * the pages (if given), attend over each sequence's cache, and - when the
- * split-KV count is above one - merge the per-split partial results with a
- * log-sum-exp combine.  Kernels run in that order on `stream`; the call
- * returns as soon as they are queued.
+ * the pages (if given), then attend over each sequence's cache.  When the
+ * split-KV count is above one, every split writes partial rows to the
+ * workspace and the last split of each (sequence, kv head) to finish merges
+ * them with the log-sum-exp combine inside the attention kernel (the split
+ * counters live in the workspace and are zeroed by the call's first kernel,
+ * so the workspace needs no initialisation).  The call returns as soon as
+ * its kernels are queued.
  * A batch whose sizes allow both decode-mode sequences (q_len * group <= 16)
- * and prefill-mode ones runs its attention as two concurrent launches: the
- * decode units on a side stream that waits on `stream` (an event after the
- * append), the prefill units on `stream`, which then waits on the side stream
- * (a second event) before the combine.  Work queued on `stream` afterwards
- * therefore sees the whole call, and a capture of `stream` takes in both
- * launches.  The side stream and its two events are created on the first such
- * call of a host thread on a device (default priority, non-blocking) and live
- * as long as the thread; a first call made while `stream` is being captured,
- * or any call with the environment variable PAGED_ATTN_SINGLE_KERNEL=1, runs
- * the attention as one unified launch instead (same results, bit for bit).
+ * and prefill-mode ones, called with an aux_stream, runs its attention as two
+ * concurrent launches: after the append on `stream`, an event forks
+ * aux_stream off to run the decode units, the prefill units run on `stream`,
+ * and `stream` then waits on a second event recorded on aux_stream.  Work
+ * queued on `stream` afterwards therefore sees the whole call, and a capture
+ * of `stream` takes in both launches.  The two events are created for the
+ * call and released once the join is queued.  Without an aux_stream (or with
+ * the environment variable PAGED_ATTN_SINGLE_KERNEL=1) the attention is one
+ * unified launch on `stream`; both plans give the same results, bit for bit.
  * Returns PA_OK or the first host-detected error (nothing launched then);
  * PA_ERR_HIP if a launch or an event operation fails.
  */
@@ -201,7 +209,9 @@ pa_status paged_kv_append(const pa_fwd_args *args, void *stream);
 
 /*
  * paged_attn_workspace_size - bytes of device workspace paged_attn_fwd needs
- * for these arguments (0 when no split-KV partials are kept).  Basis: the
+ * for these arguments (0 when no split-KV partials are kept): one counter per
+ * (sequence, kv head), then the partial rows and their log-sum-exps of every
+ * split.  Its contents need no initialisation and are scratch after the call.  Basis: the
  * small-page-size thread notes the paged call allocates nothing itself, so
  * the split-KV partials of the determine_num_splits issue's split path live
  * in caller-owned memory sized by this query.  Host only; no

@@ -59,7 +59,7 @@ class _Args(ctypes.Structure):
         ("rotary_dim", ctypes.c_int32), ("rotary_interleaved", ctypes.c_int32),
         ("rotary_rows", ctypes.c_int32), ("reserved1", ctypes.c_int32),
         ("q_row_stride", ctypes.c_int64), ("k_new_row_stride", ctypes.c_int64),
-        ("v_new_row_stride", ctypes.c_int64),
+        ("v_new_row_stride", ctypes.c_int64), ("aux_stream", ctypes.c_void_p),
     ]
 
 
@@ -290,12 +290,27 @@ def _stream_handle(stream) -> int:
     return s.cuda_stream
 
 
+_aux_streams = {}
+
+
+def default_aux_stream(device) -> torch.cuda.Stream:
+    """The binding's second stream for mixed batches on `device` (one per
+    device, default priority, created on first use and kept by the binding)."""
+    idx = torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    s = _aux_streams.get(idx)
+    if s is None:
+        s = torch.cuda.Stream(device=idx)
+        _aux_streams[idx] = s
+    return s
+
+
 def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *,
                    max_seqlen_q: int, max_seqlen_k: int = 0, k_new=None, v_new=None,
                    causal: bool = False, num_splits: int = 0, softmax_scale=None, out=None,
                    softmax_lse=None, workspace=None, rotary_cos=None, rotary_sin=None,
-                   rotary_interleaved: bool = False,
-                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                   rotary_interleaved: bool = False, stream=None,
+                   aux_stream="auto") -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged attention forward (with optional in-call append of k_new/v_new).
 
     q [total_q, Hq, D]; k_cache/v_cache [num_pages, page_size, Hkv, D] (or
@@ -306,8 +321,9 @@ def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q
     on the fused rotary embedding of q and k_new.
     Everything is queued on ``stream`` (default: torch's current stream); a
     batch that can mix decode-mode and prefill-mode sequences runs its decode
-    units on the library's side stream, forked from ``stream`` and joined back
-    into it before the call returns, so later work on ``stream`` sees the whole
+    units on ``aux_stream`` (default "auto": the binding's own second stream
+    of the device; None: one launch on ``stream``), forked from ``stream`` and
+    joined back into it by the call, so later work on ``stream`` sees the whole
     result.  Tensors the call allocates (out, softmax_lse, workspace when not
     given) are allocated on ``stream``, so the caching allocator does not hand
     them out again before the kernels queued there have finished.
@@ -321,6 +337,9 @@ def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q
                      workspace=workspace, rotary_cos=rotary_cos, rotary_sin=rotary_sin,
                      rotary_interleaved=rotary_interleaved)
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    aux = default_aux_stream(q.device) if isinstance(aux_stream, str) and aux_stream == "auto" \
+        else aux_stream
+    args.aux_stream = None if aux is None else aux.cuda_stream
     with torch.cuda.stream(s):
         if out is None:
             out = torch.empty_like(q, memory_format=torch.contiguous_format)

@@ -1,11 +1,13 @@
 // gfx950 kernels of the paged KV-cache attention forward pass.
 //
 //   kv_append_kernel   new K/V rows -> their page slots (bit copy)
+//   attn_decode_kernel decode units only: four waves, two workgroups per CU
 //   attn_fwd_kernel    one unified varlen kernel: decode units and prefill
 //                      tiles in one grid; QK^T and PV on MFMA with fp32
 //                      accumulation, online softmax, split-KV partial or final
 //                      epilogue
-//   combine_kernel     log-sum-exp merge of split-KV partials
+// With split-KV, the last split of each (sequence, kv head) to finish merges
+// the splits' partial rows inside the attention kernel (no combine launch).
 #pragma once
 
 #include "pa_common.h"
@@ -21,6 +23,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   __shared__ float sm_l[NW][kDecodeRows];           // of four in the unified kernel)
   __shared__ int s_wsum[NW];
   __shared__ int s_found[2 * kFound];
+  __shared__ int s_flag[2];                         // per half: this unit merges the splits
 
   const int g = blockIdx.x % p.hkv;
   const int wg = blockIdx.x / p.hkv;
@@ -51,10 +54,13 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     // slower (there, short units mixed with long ones keep HBM busy to the end)
     have = locate_unit<NW * 64, 2>(p, wg, u, decode, s_wsum, s_found, nullptr);
   }
-  // A half of the unified kernel without a decode unit still meets the one
-  // workgroup barrier of the other half's decode unit.
+  // A half of the unified kernel without a decode unit still meets the
+  // workgroup barriers of the other half's decode unit.
   auto idle_half = [&]() {
-    if (kUnified && decode) __syncthreads();
+    if (kUnified && decode) {
+#pragma unroll
+      for (int i = 0; i < kDecodeBarriers; ++i) __syncthreads();
+    }
   };
   if (!have) {
     idle_half();
@@ -75,15 +81,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     idle_half();
     return;
   }
-  if (decode && g == 0 && u.off == 0 && p.split_count != nullptr &&
-      (threadIdx.x & (kWaves * 64 - 1)) == 0)
-    p.split_count[u.b] = u.splits;
 
   if constexpr (!kUnified) {
     // decode-only kernel: one contiguous array, a K and a V tile per wave
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kWaves * 2 * kKeyTile * D];
-    decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si, ContigDecodeLds<kKeyTile * D>{lds},
-                               sm_m, sm_l);
+    decode_unit<DT, D, kWaves, false>(p, u.b, g, u.off, u.splits, si,
+                                      ContigDecodeLds<kKeyTile * D>{lds}, sm_m, sm_l, s_flag);
   } else {
     // unified kernel: sixteen separate 32-row slots - a K/V pair per wave of a
     // decode unit, four K and four V slots of a prefill unit (K slots at
@@ -125,11 +128,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     pool.sl[15] = lds_s15;
     if (decode) {
       if (threadIdx.x < kWaves * 64)
-        decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds<0>{pool}, sm_m,
-                                   sm_l);
+        decode_unit<DT, D, kWaves, true>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds<0>{pool},
+                                         sm_m, sm_l, s_flag);
       else
-        decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds<1>{pool},
-                                   sm_m + kWaves, sm_l + kWaves);
+        decode_unit<DT, D, kWaves, true>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds<1>{pool},
+                                         sm_m + kWaves, sm_l + kWaves, s_flag + 1);
     } else {
       const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
       if (p.geom.table != nullptr)
@@ -155,70 +158,6 @@ template <int DT, int D>
 __global__ __launch_bounds__(kUThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
   attn_fwd_body<DT, D, true>(p);
-}
-
-// ---------------------------------------------------------------------------
-// Split-KV combine: per (token, q head) row of a decode-mode sequence with
-// more than one split, lse = log(sum_s exp(lse_s)) and
-// out = sum_s exp(lse_s - lse) * o_s over the splits that saw a key; a row
-// whose splits were all empty gets out = 0, lse = -inf.  Rows of prefill
-// units and of single-split sequences were written directly and are skipped.
-// One wave per row.
-// ---------------------------------------------------------------------------
-struct CombineParams {
-  const float *o_part;
-  const float *lse_part;
-  const int32_t *split_count;
-  const int32_t *cu_seqlens_q;
-  uint16_t *out;
-  float *lse;
-  int batch, total_q, hq, group, all_decode;
-};
-
-template <int DT, int D>
-__global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
-  const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= (long)p.total_q * p.hq) return;
-  const int token = (int)(row / p.hq);
-  int lo = 0, hi = p.batch;   // largest b with cu[b] <= token
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.cu_seqlens_q[mid] <= token) lo = mid; else hi = mid;
-  }
-  const int end = min(p.cu_seqlens_q[lo + 1], p.total_q);
-  if (token >= end) return;
-  const int q_len = end - p.cu_seqlens_q[lo];
-  if (!p.all_decode && q_len * p.group > kDecodeRows) return;   // prefill row: already final
-  const int S = p.split_count[lo];
-  if (S <= 1) return;                                            // written directly
-  const long stride = (long)p.total_q * p.hq;
-  float M = kNegInf;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, p.lse_part[s * stride + row]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  constexpr int PER = D / 64;
-  float acc[PER];
-#pragma unroll
-  for (int c = 0; c < PER; ++c) acc[c] = 0.f;
-  float total = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < S; ++s) {
-      const float ls = p.lse_part[s * stride + row];
-      if (ls == kNegInf) continue;
-      const float w = fast_exp2((ls - M) * kLog2e);
-      total += w;
-      const float *src = p.o_part + (s * stride + row) * D + lane * PER;
-#pragma unroll
-      for (int c = 0; c < PER; ++c) acc[c] += w * src[c];
-    }
-  }
-  const bool empty = !(total > 0.f);
-  const float inv = empty ? 0.f : 1.f / total;
-  uint16_t *dst = p.out + row * D + lane * PER;
-#pragma unroll
-  for (int c = 0; c < PER; ++c) dst[c] = Elt<DT>::from_f32(acc[c] * inv);
-  if (lane == 0) p.lse[row] = empty ? kNegInf : M + __builtin_logf(total);
 }
 
 }  // namespace pa

@@ -1,9 +1,10 @@
 // Host dispatch and C ABI of libpaged_attn.so (declarations and contracts in
 // include/paged_attn.h).  Validates arguments, plans the launch from
 // host-static sizes only, carves the caller's workspace and queues
-// append -> attention -> combine on the caller's stream (a mixed batch forks
-// its decode units onto a side stream and joins back before the combine).
-// Never allocates device memory, frees or synchronises.
+// append -> attention on the caller's stream (a mixed batch given a second
+// stream forks its decode units onto it and joins back).  Split-KV partials
+// are merged inside the attention kernel.  Never allocates device memory,
+// frees or synchronises.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -32,7 +33,8 @@ struct Plan {
   long grid_dec = 0;      // decode-only kernel over a mixed batch's decode units
   long grid_pre = 0;      // unified kernel over its prefill units
   size_t ws_bytes = 0;
-  size_t o_part_off = 0, lse_part_off = 0, count_off = 0;
+  size_t ctr_off = 0, o_part_off = 0, lse_part_off = 0;
+  int n_ctr = 0;          // split counters, one per (sequence, kv head)
   int max_seqlen_k = 0;
 };
 
@@ -195,10 +197,12 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
     const long most = 1 + (long)a->batch * (pl.splits - 1);
     pl.max_splits = (int)std::min<long>(most, kMaxSplits);
     const size_t rows = (size_t)a->total_q * a->num_heads_q;
-    pl.o_part_off = 0;
-    pl.lse_part_off = align_up((size_t)pl.max_splits * rows * a->head_dim * sizeof(float), 256);
-    pl.count_off = align_up(pl.lse_part_off + (size_t)pl.max_splits * rows * sizeof(float), 256);
-    pl.ws_bytes = align_up(pl.count_off + (size_t)a->batch * sizeof(int32_t), 256);
+    pl.n_ctr = a->batch * a->num_heads_kv;
+    pl.ctr_off = 0;
+    pl.o_part_off = align_up((size_t)pl.n_ctr * sizeof(uint32_t), 256);
+    pl.lse_part_off =
+        align_up(pl.o_part_off + (size_t)pl.max_splits * rows * a->head_dim * sizeof(float), 256);
+    pl.ws_bytes = align_up(pl.lse_part_off + (size_t)pl.max_splits * rows * sizeof(float), 256);
   }
   return pl;
 }
@@ -258,50 +262,6 @@ pa_status check_preconditions(const pa_fwd_args *a, bool append_only, hipStream_
   return PA_OK;
 }
 
-// A mixed batch (decode-mode and prefill-mode sequences) runs as two
-// concurrent launches: the decode units in the decode-only kernel (four-wave
-// workgroups, two per CU, longest first) on a side stream, the prefill units in
-// the unified kernel on the caller's stream, joined by events.  Measured on
-// 64 decode sequences + one prefill chunk: 3-7% faster than one unified
-// launch at 32 heads x 128, equal at 12 x 64.  The side stream and the two
-// events are created once per host thread and device (default priority,
-// non-blocking) and kept for the thread's lifetime; a call made while the
-// caller's stream is being captured before they exist, or with
-// PAGED_ATTN_SINGLE_KERNEL=1, uses the one unified launch instead.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool failed = false;
-};
-
-SideStream *side_stream(hipStream_t caller) {
-  thread_local SideStream per_dev[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  SideStream &ss = per_dev[dev];
-  if (ss.s != nullptr) return &ss;
-  if (ss.failed) return nullptr;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
-    return nullptr;
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess ||
-      hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
-    // release whatever was created; the one-launch plan serves this thread
-    if (join != nullptr) (void)hipEventDestroy(join);
-    if (fork != nullptr) (void)hipEventDestroy(fork);
-    if (s != nullptr) (void)hipStreamDestroy(s);
-    ss.failed = true;
-    return nullptr;
-  }
-  ss.s = s;
-  ss.fork = fork;
-  ss.join = join;
-  return &ss;
-}
-
 bool single_kernel_forced() {
   const char *e = std::getenv("PAGED_ATTN_SINGLE_KERNEL");
   return e != nullptr && std::strcmp(e, "1") == 0;
@@ -328,9 +288,17 @@ pa::CacheGeom geom_of(const pa_fwd_args *a) {
 }
 
 // seq_mode: 0 every sequence, 1 prefill-mode sequences only, 2 decode-mode
-// sequences only (the two halves of a mixed batch's two launches)
-pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode = 0) {
-  if (a->total_q == 0 || a->max_seqlen_q == 0) return PA_OK;
+// sequences only (the two halves of a mixed batch's two launches).  `clear`
+// (n words) is zeroed by the append's first column of blocks: the split
+// counters of the attention queued after it.
+pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode = 0,
+                        uint32_t *clear = nullptr, int clear_n = 0) {
+  if (a->total_q == 0 || a->max_seqlen_q == 0) {
+    if (clear == nullptr) return PA_OK;
+    hipLaunchKernelGGL(pa::clear_kernel, dim3((unsigned)std::min<long>(cdiv(clear_n, 256), 1024)),
+                       dim3(256), 0, stream, clear, clear_n);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  }
   pa::AppendParams p;
   p.k_cache = static_cast<uint16_t *>(a->k_cache);
   p.v_cache = static_cast<uint16_t *>(a->v_cache);
@@ -351,6 +319,8 @@ pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode =
   p.tokens_per_block = std::max(1, 1024 / (2 * vec_per_row));
   p.seq_mode = seq_mode;
   p.group = a->num_heads_q / a->num_heads_kv;
+  p.clear = clear;
+  p.clear_n = clear_n;
   const int rows = seq_mode == 2 ? std::min(a->max_seqlen_q, std::max(1, pa::kDecodeRows / p.group))
                                  : a->max_seqlen_q;
   dim3 grid((unsigned)cdiv(rows, p.tokens_per_block), (unsigned)a->batch);
@@ -362,9 +332,27 @@ pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode =
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-// append (if k_new) and attention; the combine follows on `stream`
+// A mixed batch (decode-mode and prefill-mode sequences) given a second
+// stream runs its attention as two concurrent launches: the decode units in
+// the decode-only kernel (four-wave workgroups, two per CU, longest first) on
+// the caller's aux_stream, the prefill units in the unified kernel on
+// `stream`.  An event recorded on `stream` after the append forks aux_stream
+// off, a second one recorded on aux_stream after its launch joins it back.
+// The events are created for the call and released right after the join is
+// queued (the runtime keeps them until they complete).
+struct Fork {
+  hipEvent_t fork = nullptr, join = nullptr;
+  ~Fork() {
+    if (join != nullptr) (void)hipEventDestroy(join);
+    if (fork != nullptr) (void)hipEventDestroy(fork);
+  }
+};
+
+// append (if k_new, clearing the split counters on the way), then attention;
+// with split-KV the last split of each (sequence, kv head) merges the partials
 template <int DT, int D>
-pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t stream) {
+pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t stream,
+                           hipStream_t aux, bool may_fork) {
   const int group = a->num_heads_q / a->num_heads_kv;
   pa::FwdParams p;
   p.q = static_cast<const uint16_t *>(a->q);
@@ -377,9 +365,10 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   p.out = static_cast<uint16_t *>(a->out);
   p.lse = a->softmax_lse;
   char *ws = static_cast<char *>(a->workspace);
-  p.o_part = pl.splits > 1 ? reinterpret_cast<float *>(ws + pl.o_part_off) : nullptr;
-  p.lse_part = pl.splits > 1 ? reinterpret_cast<float *>(ws + pl.lse_part_off) : nullptr;
-  p.split_count = pl.splits > 1 ? reinterpret_cast<int32_t *>(ws + pl.count_off) : nullptr;
+  const bool split = pl.splits > 1;
+  p.o_part = split ? reinterpret_cast<float *>(ws + pl.o_part_off) : nullptr;
+  p.lse_part = split ? reinterpret_cast<float *>(ws + pl.lse_part_off) : nullptr;
+  p.split_ctr = split ? reinterpret_cast<uint32_t *>(ws + pl.ctr_off) : nullptr;
   p.batch = a->batch;
   p.total_q = a->total_q;
   p.hq = a->num_heads_q;
@@ -396,60 +385,44 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   p.unit_mode = 0;
   if (pl.grid > 0x7fffffffL || pl.grid_dec > 0x7fffffffL || pl.grid_pre > 0x7fffffffL)
     return PA_ERR_SHAPE;
-  SideStream *side = pl.may_mix && !single_kernel_forced() ? side_stream(stream) : nullptr;
-  const bool appends = a->k_new != nullptr;
-  if (side == nullptr && appends) {
-    const pa_status st = launch_append(a, stream);
-    if (st != PA_OK) return st;
+  // every row is appended (and the counters cleared) before any attention
+  // launch, on either stream, reads the pages
+  pa_status st = PA_OK;
+  if (a->k_new != nullptr) {
+    st = launch_append(a, stream, 0, p.split_ctr, split ? pl.n_ctr : 0);
+  } else if (split) {
+    hipLaunchKernelGGL(pa::clear_kernel, dim3((unsigned)std::min<long>(cdiv(pl.n_ctr, 256), 1024)),
+                       dim3(256), 0, stream, p.split_ctr, pl.n_ctr);
+    st = hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
+  if (st != PA_OK) return st;
   if (pl.all_decode) {
     hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(kThreads),
                        0, stream, p);
-  } else if (side != nullptr) {
-    if (hipEventRecord(side->fork, stream) != hipSuccess ||
-        hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+  } else if (pl.may_mix && may_fork && aux != nullptr && aux != stream &&
+             !single_kernel_forced()) {
+    Fork f;
+    if (hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&f.join, hipEventDisableTiming) != hipSuccess ||
+        hipEventRecord(f.fork, stream) != hipSuccess ||
+        hipStreamWaitEvent(aux, f.fork, 0) != hipSuccess)
       return PA_ERR_HIP;
-    // each launch appends the rows of its own sequences first
-    pa_status st = appends ? launch_append(a, side->s, 2) : PA_OK;
-    if (st != PA_OK) return st;
     p.unit_mode = 2;
     hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid_dec),
-                       dim3(kThreads), 0, side->s, p);
-    if (hipGetLastError() != hipSuccess || hipEventRecord(side->join, side->s) != hipSuccess)
+                       dim3(kThreads), 0, aux, p);
+    if (hipGetLastError() != hipSuccess || hipEventRecord(f.join, aux) != hipSuccess)
       return PA_ERR_HIP;
-    st = appends ? launch_append(a, stream, 1) : PA_OK;
-    if (st != PA_OK) return st;
     p.unit_mode = 1;
     hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid_pre),
                        dim3(pa::kUThreads), 0, stream, p);
-    if (hipGetLastError() != hipSuccess || hipStreamWaitEvent(stream, side->join, 0) != hipSuccess)
-      return PA_ERR_HIP;
+    // join even when the launch failed, so aux_stream is never left forked
+    const bool launched = hipGetLastError() == hipSuccess;
+    if (hipStreamWaitEvent(stream, f.join, 0) != hipSuccess || !launched) return PA_ERR_HIP;
   } else {
     hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(pa::kUThreads), 0,
                        stream, p);
   }
-  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-  if (pl.splits > 1) {
-    pa::CombineParams c;
-    c.o_part = p.o_part;
-    c.lse_part = p.lse_part;
-    c.split_count = p.split_count;
-    c.cu_seqlens_q = a->cu_seqlens_q;
-    c.out = p.out;
-    c.lse = p.lse;
-    c.batch = a->batch;
-    c.total_q = a->total_q;
-    c.hq = a->num_heads_q;
-    c.group = group;
-    c.all_decode = pl.all_decode;
-    const long rows = (long)a->total_q * a->num_heads_q;
-    const long blocks = cdiv(rows, pa::kWaves);
-    if (blocks > 0x7fffffffL) return PA_ERR_SHAPE;
-    hipLaunchKernelGGL((pa::combine_kernel<DT, D>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, c);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-  }
-  return PA_OK;
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // namespace
@@ -515,12 +488,13 @@ pa_status paged_attn_fwd(const pa_fwd_args *args, void *stream) {
   if (pl.ws_bytes > 0 && (args->workspace == nullptr || args->workspace_bytes < pl.ws_bytes))
     return PA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t aux = static_cast<hipStream_t>(args->aux_stream);
   const bool bf16 = args->dtype == PA_BF16;
   if (args->head_dim == 128)
-    return bf16 ? launch_attention<pa::kBF16, 128>(args, pl, s)
-                : launch_attention<pa::kF16, 128>(args, pl, s);
-  return bf16 ? launch_attention<pa::kBF16, 64>(args, pl, s)
-              : launch_attention<pa::kF16, 64>(args, pl, s);
+    return bf16 ? launch_attention<pa::kBF16, 128>(args, pl, s, aux, true)
+                : launch_attention<pa::kF16, 128>(args, pl, s, aux, true);
+  return bf16 ? launch_attention<pa::kBF16, 64>(args, pl, s, aux, true)
+              : launch_attention<pa::kF16, 64>(args, pl, s, aux, true);
 }
 
 const char *paged_attn_status_string(int32_t status) {

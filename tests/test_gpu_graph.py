@@ -1,6 +1,6 @@
 """Graph capture of one paged_attn_fwd call.
 
-One call (append + unified attention + split combine) on fixed device buffers
+One call (append + attention with its split-KV merge) on fixed device buffers
 is captured once into a HIP graph and replayed with different batches loaded
 into the same buffers: prefill chunks and decode sequences of different
 lengths, with the unused sequence slots padded as (0, 0) (no new tokens, empty
@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 SLOTS, T_STATIC, MAXQ, HQ, HKV, D, P = 6, 96, 64, 8, 2, 128, 16
 WIDTH = 80                      # table entries per slot: keys per slot <= 1280
-SPLITS = 3                      # forced budget: the combine kernel is in the graph too
+SPLITS = 3                      # forced budget: the split merge is in the graph too
 
 # (q_lens, cache_seqlens) per batch; trailing slots are (0, 0) padding
 BATCHES = [
@@ -55,14 +55,17 @@ def _call(buf):
     pa.paged_attn_fwd(buf["q"], buf["k_cache"], buf["v_cache"], buf["table"], buf["seqlens"],
                       buf["cu"], max_seqlen_q=MAXQ, max_seqlen_k=WIDTH * P, k_new=buf["k_new"],
                       v_new=buf["v_new"], causal=True, num_splits=SPLITS, out=buf["out"],
-                      softmax_lse=buf["lse"], workspace=buf["ws"])
+                      softmax_lse=buf["lse"], workspace=buf["ws"], aux_stream=buf["aux"])
 
 
 def _snapshot(buf):
     return {k: buf[k].clone() for k in ("out", "lse", "k_cache", "v_cache")}
 
 
-def test_graph_replays_match_eager_calls():
+# "auto": the binding's second stream, so the captured call forks the decode
+# units off and joins them back; None: one launch on the captured stream
+@pytest.mark.parametrize("aux", ["auto", None])
+def test_graph_replays_match_eager_calls(aux):
     assert torch.cuda.is_available()
     rng = np.random.default_rng(5150)
     num_pages = SLOTS * WIDTH
@@ -90,6 +93,7 @@ def test_graph_replays_match_eager_calls():
     need = pa.paged_attn_workspace_size(args)
     assert need > 0, "a forced split budget needs a workspace"
     buf["ws"] = torch.empty(need, dtype=torch.uint8, device="cuda")
+    buf["aux"] = aux
 
     # eager results of every batch on the static buffers
     eager = []

@@ -224,9 +224,11 @@ def test_unified_varlen_with_prefix():
 
 
 # A batch that can mix decode-mode and prefill-mode sequences runs as two
-# concurrent launches (decode units on a side stream); PAGED_ATTN_SINGLE_KERNEL=1
-# keeps the one unified launch.  Both plans run the same unit code, so they
-# must agree bit for bit, and the one-launch plan keeps its oracle parity.
+# concurrent launches when the call has a second stream (decode units on
+# aux_stream); without one (aux_stream=None), or with
+# PAGED_ATTN_SINGLE_KERNEL=1, it is one unified launch.  Both plans run the
+# same unit code, so they must agree bit for bit, and the one-launch plan
+# keeps its oracle parity.
 @pytest.mark.parametrize("nq,heads,hd", [(100, 32, 128), (1000, 12, 64)])
 def test_unified_varlen_one_launch(nq, heads, hd, monkeypatch):
     monkeypatch.setenv("PAGED_ATTN_SINGLE_KERNEL", "1")
@@ -237,7 +239,7 @@ def test_unified_varlen_one_launch(nq, heads, hd, monkeypatch):
                                   wl.unified_varlen(100, heads=12, head_dim=64),
                                   wl.multi_token_decode(3, 700, 2)],
                          ids=lambda c: c.name)
-def test_two_launches_equal_one_launch(case, monkeypatch):
+def test_two_launches_equal_one_launch(case):
     if case.name.startswith("multi_token"):
         # one prefill-mode sequence among decode-mode ones
         case.q_lens = [2, 40, 2]
@@ -247,13 +249,9 @@ def test_two_launches_equal_one_launch(case, monkeypatch):
     for s in (None, 2):
         got = {}
         for plan in ("two", "one"):
-            if plan == "one":
-                monkeypatch.setenv("PAGED_ATTN_SINGLE_KERNEL", "1")
-            else:
-                monkeypatch.delenv("PAGED_ATTN_SINGLE_KERNEL", raising=False)
             inp.k_cache.copy_(kc0)
             inp.v_cache.copy_(vc0)
-            out, lse = gpu_call(inp, num_splits=s)
+            out, lse = gpu_call(inp, num_splits=s, aux_stream="auto" if plan == "two" else None)
             got[plan] = (out.clone(), lse.clone(), inp.k_cache.clone(), inp.v_cache.clone())
         for name, a, b in zip(("out", "lse", "k_cache", "v_cache"), got["two"], got["one"]):
             bits = torch.int16 if a.element_size() == 2 else torch.int32
