@@ -173,18 +173,16 @@ typedef struct pa_fwd_args {
 
 /*
  * paged_attn_fwd - the whole forward call on `stream`: append k_new/v_new into
- * the pages (if given), then attend over each sequence's cache.  When the
- * split-KV count is above one, every split writes partial rows to the
- * workspace and the last split of each (sequence, kv head) to finish merges
- * them with the log-sum-exp combine inside the attention kernel (the split
- * counters live in the workspace and are zeroed by the call's first kernel,
- * so the workspace needs no initialisation).  The call returns as soon as
- * its kernels are queued.
+ * the pages (if given), attend over each sequence's cache, and - when the
+ * split-KV count is above one - merge the per-split partial rows with a
+ * log-sum-exp combine.  Kernels run in that order; the call returns as soon
+ * as they are queued.
  * A batch whose sizes allow both decode-mode sequences (q_len * group <= 16)
  * and prefill-mode ones, called with an aux_stream, runs its attention as two
  * concurrent launches: after the append on `stream`, an event forks
  * aux_stream off to run the decode units, the prefill units run on `stream`,
- * and `stream` then waits on a second event recorded on aux_stream.  Work
+ * and `stream` then waits on a second event recorded on aux_stream before
+ * the combine.  Work
  * queued on `stream` afterwards therefore sees the whole call, and a capture
  * of `stream` takes in both launches.  The two events are created for the
  * call and released once the join is queued.  Without an aux_stream (or with
@@ -209,9 +207,9 @@ pa_status paged_kv_append(const pa_fwd_args *args, void *stream);
 
 /*
  * paged_attn_workspace_size - bytes of device workspace paged_attn_fwd needs
- * for these arguments (0 when no split-KV partials are kept): one counter per
- * (sequence, kv head), then the partial rows and their log-sum-exps of every
- * split.  Its contents need no initialisation and are scratch after the call.  Basis: the
+ * for these arguments (0 when no split-KV partials are kept): the partial
+ * rows and log-sum-exps of every split and each row's split count.  Its
+ * contents need no initialisation and are scratch after the call.  Basis: the
  * small-page-size thread notes the paged call allocates nothing itself, so
  * the split-KV partials of the determine_num_splits issue's split path live
  * in caller-owned memory sized by this query.  Host only; no

@@ -30,8 +30,8 @@ struct FwdParams {
   float *lse;
   float *o_part;       // [max_splits, total_q, hq, D] fp32 (num_splits > 1)
   float *lse_part;     // [max_splits, total_q, hq]
-  uint32_t *split_ctr; // [batch * hkv]: splits of (sequence, kv head) finished so far;
-                       // zero when the attention starts (num_splits > 1)
+  int32_t *row_splits; // [total_q, hq] (num_splits > 1): splits that wrote partials for
+                       // the row, 1 for a row written directly (single split, prefill)
   int batch, total_q, hq, hkv, group;
   int appended, causal, num_splits;
   float scale_log2;    // softmax scale * log2(e)
@@ -55,15 +55,7 @@ struct AppendParams {
                        // (q_len * group <= kDecodeRows)
   Rotary rot;          // rotary embedding of the new keys (rot.cos == nullptr: none)
   long kn_stride, vn_stride;   // elements between consecutive tokens' k_new / v_new rows
-  uint32_t *clear;     // words zeroed on the way (the split counters of the attention
-  int clear_n;         // that follows on the stream), or nullptr
 };
-
-// Zeroes n words: the split counters of an attention launch that has no
-// append in front of it to do so.
-__global__ __launch_bounds__(256) void clear_kernel(uint32_t *p, int n) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
-}
 
 // ---------------------------------------------------------------------------
 // Append (vLLM's reshape_and_cache; the in-call k=/v= of flash-attention's
@@ -76,12 +68,6 @@ __global__ __launch_bounds__(256) void clear_kernel(uint32_t *p, int n) {
 template <int DT>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
   const int b = blockIdx.y;
-  // the first column of blocks zeroes the split counters of the attention that
-  // follows (before any early exit below)
-  if (p.clear != nullptr && blockIdx.x == 0) {
-    for (int i = b * kThreads + threadIdx.x; i < p.clear_n; i += gridDim.y * kThreads)
-      p.clear[i] = 0u;
-  }
   const int cu_b = p.cu_seqlens_q[b];
   // rows past total_q (malformed cu_seqlens_q) are never touched
   const int q_len = max(0, min(p.cu_seqlens_q[b + 1], p.total_q) - cu_b);

@@ -28,36 +28,14 @@ namespace pa {
 //   S^T = K Q^T  16x16x32 MFMA, keys on M: each lane's probabilities are
 //                already the B operand of the PV product;
 //   O^T += V^T P^T 16x16x32 MFMA on key-contiguous V^T from transposing reads.
-// The waves' (max, sum, O) states merge through LDS at the end, after a
-// workgroup barrier; a split writes partial rows, and the last split of the
-// (sequence, kv head) to finish merges them (see the epilogue).
+// The waves' (max, sum, O) states merge through LDS at the end, after the
+// unit's only workgroup barrier (a half without a unit meets it on its own).
 // ---------------------------------------------------------------------------
-// Barriers: one after the key loop; with more than one split two more around
-// the counter of the fused combine - always, when kUniformBarriers (a half of
-// the unified kernel, whose other half may need them); kDecodeBarriers in all.
-constexpr int kDecodeBarriers = 3;
-
-// the CH fp32 values acc[c] * inv rounded to the element type, one row chunk
-template <int DT, int CH>
-__device__ inline void store_out_row(uint16_t *dst, const float (&acc)[CH], float inv) {
-  if constexpr (CH == 8) {
-    u32x4 pk;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pk[e] = pack2<DT>(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-    store16(dst, pk);
-  } else {
-    u32x2 pk;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) pk[e] = pack2<DT>(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-    *reinterpret_cast<u32x2 *>(dst) = pk;
-  }
-}
-
-template <int DT, int D, int NW, bool kUniformBarriers, class Lds>
+template <int DT, int D, int NW, class Lds>
 __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, const int g,
                                             const int split, const int S_b, const SeqInfo si,
                                             const Lds &lds, float (*sm_m)[kDecodeRows],
-                                            float (*sm_l)[kDecodeRows], int *s_flag) {
+                                            float (*sm_l)[kDecodeRows]) {
   constexpr int DS = D / 32;       // k-steps of S^T (32 dims each)
   constexpr int DB = D / 16;       // 16-dim blocks of O^T
   constexpr int CPR = D / 8;       // 16-byte chunks per K/V row
@@ -303,92 +281,55 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
   constexpr int CH = D / 16;       // dims per thread in the write-out
   const int orow = tid >> 4;       // 0..15
   const int oc = tid & 15;
-  const bool active = orow < rows_b;
+  if (orow >= rows_b) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][orow]);
+  float acc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc[c] = 0.f;
+  float L = 0.f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = fast_exp2(sm_m[w][orow] - M);   // 0 for waves that saw nothing
+      L += wt * sm_l[w][orow];
+      const float *src = reinterpret_cast<const float *>(lds.k_const(w)) + orow * D + oc * CH;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) acc[c] += wt * src[c];
+    }
+  }
+  const bool empty = !(L > 0.f);
+  const float inv = empty ? 0.f : 1.f / L;
+  const float lse_val = empty ? kNegInf : (M + __builtin_log2f(L)) * kLn2;
   const int tk = orow / group;
   const int hp = g * group + (orow - tk * group);
   const long ridx = (long)(si.cu_b + tk) * p.hq + hp;
-  const long stride = (long)p.total_q * p.hq;   // rows of one split's partials
-  if (active) {
-    float M = kNegInf;
+  if (S_b == 1) {
+    uint16_t *dst = p.out + ridx * D + oc * CH;
+    if constexpr (CH == 8) {
+      u32x4 pk;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][orow]);
-    float acc[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) acc[c] = 0.f;
-    float L = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float wt = fast_exp2(sm_m[w][orow] - M);   // 0 for waves that saw nothing
-        L += wt * sm_l[w][orow];
-        const float *src = reinterpret_cast<const float *>(lds.k_const(w)) + orow * D + oc * CH;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) acc[c] += wt * src[c];
-      }
-    }
-    const bool empty = !(L > 0.f);
-    const float inv = empty ? 0.f : 1.f / L;
-    const float lse_val = empty ? kNegInf : (M + __builtin_log2f(L)) * kLn2;
-    if (S_b == 1) {
-      store_out_row<DT, CH>(p.out + ridx * D + oc * CH, acc, inv);
-      if (oc == 0) p.lse[ridx] = lse_val;
+      for (int e = 0; e < 4; ++e) pk[e] = pack2<DT>(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+      store16(dst, pk);
     } else {
-      const long pidx = (long)split * stride + ridx;
-      float *dst = p.o_part + pidx * D + oc * CH;
+      u32x2 pk;
 #pragma unroll
-      for (int c = 0; c < CH; c += 4)
-        *reinterpret_cast<f32x4 *>(dst + c) =
-            f32x4{acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
-      if (oc == 0) p.lse_part[pidx] = lse_val;
+      for (int e = 0; e < 2; ++e) pk[e] = pack2<DT>(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+      *reinterpret_cast<u32x2 *>(dst) = pk;
     }
+    if (oc == 0) p.lse[ridx] = lse_val;
+  } else {
+    const long pidx = (long)split * p.total_q * p.hq + ridx;
+    float *dst = p.o_part + pidx * D + oc * CH;
+#pragma unroll
+    for (int c = 0; c < CH; c += 4)
+      *reinterpret_cast<f32x4 *>(dst + c) =
+          f32x4{acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
+    if (oc == 0) p.lse_part[pidx] = lse_val;
   }
-
-  // ---- split-KV combine, fused: the last split of (sequence, kv head) to
-  // finish merges every split's partial rows (the log-sum-exp merge of the
-  // determine_num_splits issue's split path).  The unit's partial stores are
-  // released at device scope before its counter increment, and the merging
-  // unit acquires before reading the others', so partials written by
-  // workgroups on other XCDs (other L2 caches) are seen.  A half of the
-  // unified kernel meets these two barriers whatever its split count, as the
-  // other half may need them.
-  if (kUniformBarriers || S_b > 1) {
-    __syncthreads();
-    if (S_b > 1 && tid == 0) {
-      const uint32_t done = __hip_atomic_fetch_add(p.split_ctr + (long)b * p.hkv + g, 1u,
-                                                   __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      *s_flag = done == (uint32_t)(S_b - 1);
-    }
-    __syncthreads();
-    if (S_b > 1 && *s_flag) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      if (active) {
-        float M = kNegInf;
-        for (int sp = 0; sp < S_b; ++sp) M = fmaxf(M, p.lse_part[sp * stride + ridx]);
-        float acc[CH];
-#pragma unroll
-        for (int c = 0; c < CH; ++c) acc[c] = 0.f;
-        float total = 0.f;
-        if (M != kNegInf) {
-          for (int sp = 0; sp < S_b; ++sp) {
-            const float ls = p.lse_part[sp * stride + ridx];
-            if (ls == kNegInf) continue;   // a split that saw no key
-            const float w = fast_exp2((ls - M) * kLog2e);
-            total += w;
-            const float *src = p.o_part + (sp * stride + ridx) * D + oc * CH;
-#pragma unroll
-            for (int c = 0; c < CH; c += 4) {
-              const f32x4 v = *reinterpret_cast<const f32x4 *>(src + c);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[c + e] += w * v[e];
-            }
-          }
-        }
-        const bool empty = !(total > 0.f);
-        store_out_row<DT, CH>(p.out + ridx * D + oc * CH, acc, empty ? 0.f : 1.f / total);
-        if (oc == 0) p.lse[ridx] = empty ? kNegInf : M + __builtin_logf(total);
-      }
-    }
-  }
+  // the row's split count, for the combine (split 0 of every decode sequence)
+  if (p.row_splits != nullptr && split == 0 && oc == 0) p.row_splits[ridx] = S_b;
 }
 
 }  // namespace pa

@@ -1,13 +1,11 @@
 // gfx950 kernels of the paged KV-cache attention forward pass.
 //
 //   kv_append_kernel   new K/V rows -> their page slots (bit copy)
-//   attn_decode_kernel decode units only: four waves, two workgroups per CU
 //   attn_fwd_kernel    one unified varlen kernel: decode units and prefill
 //                      tiles in one grid; QK^T and PV on MFMA with fp32
 //                      accumulation, online softmax, split-KV partial or final
 //                      epilogue
-// With split-KV, the last split of each (sequence, kv head) to finish merges
-// the splits' partial rows inside the attention kernel (no combine launch).
+//   combine_kernel     log-sum-exp merge of split-KV partials
 #pragma once
 
 #include "pa_common.h"
@@ -23,7 +21,6 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   __shared__ float sm_l[NW][kDecodeRows];           // of four in the unified kernel)
   __shared__ int s_wsum[NW];
   __shared__ int s_found[2 * kFound];
-  __shared__ int s_flag[2];                         // per half: this unit merges the splits
 
   const int g = blockIdx.x % p.hkv;
   const int wg = blockIdx.x / p.hkv;
@@ -54,13 +51,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     // slower (there, short units mixed with long ones keep HBM busy to the end)
     have = locate_unit<NW * 64, 2>(p, wg, u, decode, s_wsum, s_found, nullptr);
   }
-  // A half of the unified kernel without a decode unit still meets the
-  // workgroup barriers of the other half's decode unit.
+  // A half of the unified kernel without a decode unit still meets the one
+  // workgroup barrier of the other half's decode unit.
   auto idle_half = [&]() {
-    if (kUnified && decode) {
-#pragma unroll
-      for (int i = 0; i < kDecodeBarriers; ++i) __syncthreads();
-    }
+    if (kUnified && decode) __syncthreads();
   };
   if (!have) {
     idle_half();
@@ -85,8 +79,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   if constexpr (!kUnified) {
     // decode-only kernel: one contiguous array, a K and a V tile per wave
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kWaves * 2 * kKeyTile * D];
-    decode_unit<DT, D, kWaves, false>(p, u.b, g, u.off, u.splits, si,
-                                      ContigDecodeLds<kKeyTile * D>{lds}, sm_m, sm_l, s_flag);
+    decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si, ContigDecodeLds<kKeyTile * D>{lds},
+                               sm_m, sm_l);
   } else {
     // unified kernel: sixteen separate 32-row slots - a K/V pair per wave of a
     // decode unit, four K and four V slots of a prefill unit (K slots at
@@ -128,11 +122,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     pool.sl[15] = lds_s15;
     if (decode) {
       if (threadIdx.x < kWaves * 64)
-        decode_unit<DT, D, kWaves, true>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds<0>{pool},
-                                         sm_m, sm_l, s_flag);
+        decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds<0>{pool}, sm_m,
+                                   sm_l);
       else
-        decode_unit<DT, D, kWaves, true>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds<1>{pool},
-                                         sm_m + kWaves, sm_l + kWaves, s_flag + 1);
+        decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si, PoolDecodeLds<1>{pool},
+                                   sm_m + kWaves, sm_l + kWaves);
     } else {
       const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
       if (p.geom.table != nullptr)
@@ -158,6 +152,79 @@ template <int DT, int D>
 __global__ __launch_bounds__(kUThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p) {
   attn_fwd_body<DT, D, true>(p);
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV combine: per (token, q head) row written as partials by more than
+// one split, lse = log(sum_s exp(lse_s)) and out = sum_s exp(lse_s - lse) *
+// o_s over the splits that saw a key; a row whose splits were all empty gets
+// out = 0, lse = -inf.  One wave per row.  The attention kernel recorded each
+// row's split count (1 for rows it wrote directly), so a wave needs two
+// rounds of loads: that count with cu_seqlens_q[batch] (rows past it belong
+// to no sequence), then every split's partial row at once.
+// ---------------------------------------------------------------------------
+struct CombineParams {
+  const float *o_part;
+  const float *lse_part;
+  const int32_t *row_splits;
+  const int32_t *cu_seqlens_q;
+  uint16_t *out;
+  float *lse;
+  int batch, total_q, hq, max_splits;
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (row >= (long)p.total_q * p.hq) return;
+  const int rows_end = min(p.cu_seqlens_q[p.batch], p.total_q);
+  const int S = min(p.row_splits[row], p.max_splits);   // clamped: never past the partials
+  if (row / p.hq >= rows_end || S <= 1) return;          // no sequence, or written directly
+  const long stride = (long)p.total_q * p.hq;
+  constexpr int PER = D / 64;
+  // chunks of eight splits: their lses and partial rows (PER dims per lane)
+  // are all loaded before any is used, and chunks merge by a running maximum
+  constexpr int CK = 8;
+  float M = kNegInf, total = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) acc[c] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += CK) {
+    float ls[CK], v[CK][PER];
+#pragma unroll
+    for (int j = 0; j < CK; ++j) {
+      const long sj = min(s0 + j, S - 1);   // past the last split: re-read it, unused
+      ls[j] = p.lse_part[sj * stride + row];
+      const float *src = p.o_part + (sj * stride + row) * D + lane * PER;
+#pragma unroll
+      for (int c = 0; c < PER; ++c) v[j][c] = src[c];
+    }
+    float cm = M;
+#pragma unroll
+    for (int j = 0; j < CK; ++j)
+      if (s0 + j < S) cm = fmaxf(cm, ls[j]);
+    if (cm == kNegInf) continue;   // every split so far saw no key
+    const float r = M == kNegInf ? 0.f : fast_exp2((M - cm) * kLog2e);
+    total *= r;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) acc[c] *= r;
+#pragma unroll
+    for (int j = 0; j < CK; ++j) {
+      if (s0 + j >= S || ls[j] == kNegInf) continue;   // a split that saw no key
+      const float w = fast_exp2((ls[j] - cm) * kLog2e);
+      total += w;
+#pragma unroll
+      for (int c = 0; c < PER; ++c) acc[c] += w * v[j][c];
+    }
+    M = cm;
+  }
+  const bool empty = !(total > 0.f);
+  const float inv = empty ? 0.f : 1.f / total;
+  uint16_t *dst = p.out + row * D + lane * PER;
+#pragma unroll
+  for (int c = 0; c < PER; ++c) dst[c] = Elt<DT>::from_f32(acc[c] * inv);
+  if (lane == 0) p.lse[row] = empty ? kNegInf : M + __builtin_logf(total);
 }
 
 }  // namespace pa

@@ -517,6 +517,8 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     }
   }
   if (hh == 0) p.lse[ridx] = empty ? kNegInf : (m_run * c2 + __builtin_log2f(L)) * kLn2;
+  // written directly: the combine that follows a split batch skips the row
+  if (hh == 0 && p.row_splits != nullptr) p.row_splits[ridx] = 1;
 }
 
 }  // namespace pa

@@ -2,9 +2,8 @@
 // include/paged_attn.h).  Validates arguments, plans the launch from
 // host-static sizes only, carves the caller's workspace and queues
 // append -> attention on the caller's stream (a mixed batch given a second
-// stream forks its decode units onto it and joins back).  Split-KV partials
-// are merged inside the attention kernel.  Never allocates device memory,
-// frees or synchronises.
+// stream forks its decode units onto it and joins back before the split-KV
+// combine).  Never allocates device memory, frees or synchronises.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -33,8 +32,7 @@ struct Plan {
   long grid_dec = 0;      // decode-only kernel over a mixed batch's decode units
   long grid_pre = 0;      // unified kernel over its prefill units
   size_t ws_bytes = 0;
-  size_t ctr_off = 0, o_part_off = 0, lse_part_off = 0;
-  int n_ctr = 0;          // split counters, one per (sequence, kv head)
+  size_t o_part_off = 0, lse_part_off = 0, rsplit_off = 0;
   int max_seqlen_k = 0;
 };
 
@@ -197,12 +195,10 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
     const long most = 1 + (long)a->batch * (pl.splits - 1);
     pl.max_splits = (int)std::min<long>(most, kMaxSplits);
     const size_t rows = (size_t)a->total_q * a->num_heads_q;
-    pl.n_ctr = a->batch * a->num_heads_kv;
-    pl.ctr_off = 0;
-    pl.o_part_off = align_up((size_t)pl.n_ctr * sizeof(uint32_t), 256);
-    pl.lse_part_off =
-        align_up(pl.o_part_off + (size_t)pl.max_splits * rows * a->head_dim * sizeof(float), 256);
-    pl.ws_bytes = align_up(pl.lse_part_off + (size_t)pl.max_splits * rows * sizeof(float), 256);
+    pl.o_part_off = 0;
+    pl.lse_part_off = align_up((size_t)pl.max_splits * rows * a->head_dim * sizeof(float), 256);
+    pl.rsplit_off = align_up(pl.lse_part_off + (size_t)pl.max_splits * rows * sizeof(float), 256);
+    pl.ws_bytes = align_up(pl.rsplit_off + rows * sizeof(int32_t), 256);
   }
   return pl;
 }
@@ -288,17 +284,9 @@ pa::CacheGeom geom_of(const pa_fwd_args *a) {
 }
 
 // seq_mode: 0 every sequence, 1 prefill-mode sequences only, 2 decode-mode
-// sequences only (the two halves of a mixed batch's two launches).  `clear`
-// (n words) is zeroed by the append's first column of blocks: the split
-// counters of the attention queued after it.
-pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode = 0,
-                        uint32_t *clear = nullptr, int clear_n = 0) {
-  if (a->total_q == 0 || a->max_seqlen_q == 0) {
-    if (clear == nullptr) return PA_OK;
-    hipLaunchKernelGGL(pa::clear_kernel, dim3((unsigned)std::min<long>(cdiv(clear_n, 256), 1024)),
-                       dim3(256), 0, stream, clear, clear_n);
-    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
-  }
+// sequences only
+pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode = 0) {
+  if (a->total_q == 0 || a->max_seqlen_q == 0) return PA_OK;
   pa::AppendParams p;
   p.k_cache = static_cast<uint16_t *>(a->k_cache);
   p.v_cache = static_cast<uint16_t *>(a->v_cache);
@@ -319,8 +307,6 @@ pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode =
   p.tokens_per_block = std::max(1, 1024 / (2 * vec_per_row));
   p.seq_mode = seq_mode;
   p.group = a->num_heads_q / a->num_heads_kv;
-  p.clear = clear;
-  p.clear_n = clear_n;
   const int rows = seq_mode == 2 ? std::min(a->max_seqlen_q, std::max(1, pa::kDecodeRows / p.group))
                                  : a->max_seqlen_q;
   dim3 grid((unsigned)cdiv(rows, p.tokens_per_block), (unsigned)a->batch);
@@ -348,8 +334,7 @@ struct Fork {
   }
 };
 
-// append (if k_new, clearing the split counters on the way), then attention;
-// with split-KV the last split of each (sequence, kv head) merges the partials
+// append (if k_new), attention, and with split-KV the combine of the partials
 template <int DT, int D>
 pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t stream,
                            hipStream_t aux, bool may_fork) {
@@ -368,7 +353,7 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   const bool split = pl.splits > 1;
   p.o_part = split ? reinterpret_cast<float *>(ws + pl.o_part_off) : nullptr;
   p.lse_part = split ? reinterpret_cast<float *>(ws + pl.lse_part_off) : nullptr;
-  p.split_ctr = split ? reinterpret_cast<uint32_t *>(ws + pl.ctr_off) : nullptr;
+  p.row_splits = split ? reinterpret_cast<int32_t *>(ws + pl.rsplit_off) : nullptr;
   p.batch = a->batch;
   p.total_q = a->total_q;
   p.hq = a->num_heads_q;
@@ -385,17 +370,12 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   p.unit_mode = 0;
   if (pl.grid > 0x7fffffffL || pl.grid_dec > 0x7fffffffL || pl.grid_pre > 0x7fffffffL)
     return PA_ERR_SHAPE;
-  // every row is appended (and the counters cleared) before any attention
-  // launch, on either stream, reads the pages
-  pa_status st = PA_OK;
+  // every row is appended before any attention launch, on either stream,
+  // reads the pages
   if (a->k_new != nullptr) {
-    st = launch_append(a, stream, 0, p.split_ctr, split ? pl.n_ctr : 0);
-  } else if (split) {
-    hipLaunchKernelGGL(pa::clear_kernel, dim3((unsigned)std::min<long>(cdiv(pl.n_ctr, 256), 1024)),
-                       dim3(256), 0, stream, p.split_ctr, pl.n_ctr);
-    st = hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+    const pa_status st = launch_append(a, stream);
+    if (st != PA_OK) return st;
   }
-  if (st != PA_OK) return st;
   if (pl.all_decode) {
     hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(kThreads),
                        0, stream, p);
@@ -422,7 +402,27 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
     hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(pa::kUThreads), 0,
                        stream, p);
   }
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  if (split) {
+    pa::CombineParams c;
+    c.o_part = p.o_part;
+    c.lse_part = p.lse_part;
+    c.row_splits = p.row_splits;
+    c.cu_seqlens_q = a->cu_seqlens_q;
+    c.out = p.out;
+    c.lse = p.lse;
+    c.batch = a->batch;
+    c.total_q = a->total_q;
+    c.hq = a->num_heads_q;
+    c.max_splits = pl.max_splits;
+    const long rows = (long)a->total_q * a->num_heads_q;
+    const long blocks = cdiv(rows, pa::kWaves);
+    if (blocks > 0x7fffffffL) return PA_ERR_SHAPE;
+    hipLaunchKernelGGL((pa::combine_kernel<DT, D>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, c);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
 }
 
 }  // namespace
