@@ -31,7 +31,8 @@
  *    launch failure returns PA_ERR_HIP.  Device-side faults are asynchronous
  *    and surface at the caller's next synchronisation.  No exception crosses
  *    the ABI.  The library keeps no mutable global state except a per-device
- *    cache of the compute-unit count.
+ *    cache of the compute-unit count and, for paged_attn_fwd_noalloc only,
+ *    its static scratch array and that array's per-device address.
  *  - Element types: q, caches, k_new, v_new and out share one 16-bit float
  *    type (fp16 or bf16).  Accumulation is fp32; out is rounded to nearest
  *    even once; softmax_lse is fp32, natural log.
@@ -58,8 +59,10 @@ typedef enum pa_status {
   PA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
   PA_ERR_ALIGN = 7,       /* a buffer read or written in 16-byte vectors (q, caches,
                              k_new, v_new, out, rotary tables) is not 16-byte aligned */
-  PA_ERR_PRECONDITION = 8 /* device metadata breaks a precondition; only reported when
+  PA_ERR_PRECONDITION = 8,/* device metadata breaks a precondition; only reported when
                              the environment sets PAGED_ATTN_DEBUG=1 (see below) */
+  PA_ERR_SCRATCH = 9      /* paged_attn_fwd_noalloc: the call's split-KV scratch exceeds
+                             the library's static 64 MiB array */
 } pa_status;
 
 typedef enum pa_dtype { PA_F16 = 0, PA_BF16 = 1 } pa_dtype;
@@ -192,6 +195,25 @@ typedef struct pa_fwd_args {
  * PA_ERR_HIP if a launch or an event operation fails.
  */
 pa_status paged_attn_fwd(const pa_fwd_args *args, void *stream);
+
+/*
+ * paged_attn_fwd_noalloc - paged_attn_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, kernels and results (bit for bit)
+ * as paged_attn_fwd, except that args->workspace / workspace_bytes and
+ * args->aux_stream are ignored: the split-KV scratch is a static device array
+ * of the library (64 MiB = 67108864 bytes), one per device, held from the library's load on the device until the process ends,
+ * and a mixed batch always runs as one launch on `stream`.  The call makes no
+ * allocation of any kind (it creates no events either) and never
+ * synchronises; PAGED_ATTN_DEBUG is not honoured here.  A call whose plan
+ * needs more scratch than the array holds returns PA_ERR_SCRATCH before any
+ * launch (paged_attn_workspace_size gives the need).  Every call on a device
+ * shares that device's array, and the array keeps the last call's contents
+ * (nothing in it needs to start at zero): calls that overlap on one device
+ * (concurrent streams, or several host threads) race on it and must be
+ * serialised by the caller.
+ */
+pa_status paged_attn_fwd_noalloc(const pa_fwd_args *args, void *stream);
 
 /*
  * paged_kv_append - the append step alone (vLLM's reshape_and_cache): writes

@@ -22,13 +22,16 @@ import torch
 from . import _build
 
 __all__ = [
-    "PagedAttnError", "paged_attn_fwd", "paged_kv_append", "paged_attn_workspace_size",
+    "PagedAttnError", "paged_attn_fwd", "paged_attn_fwd_noalloc", "paged_kv_append", "paged_attn_workspace_size",
     "paged_attn_splits_for", "paged_attn_num_splits", "paged_attn_status_string", "library_path",
     "EXPORTED_SYMBOLS",
 ]
 
-EXPORTED_SYMBOLS = ("paged_attn_fwd", "paged_kv_append", "paged_attn_workspace_size",
-                    "paged_attn_splits_for", "paged_attn_num_splits", "paged_attn_status_string")
+EXPORTED_SYMBOLS = ("paged_attn_fwd", "paged_attn_fwd_noalloc", "paged_kv_append",
+                    "paged_attn_workspace_size", "paged_attn_splits_for", "paged_attn_num_splits",
+                    "paged_attn_status_string")
+PA_ERR_SCRATCH = 9
+NOALLOC_SCRATCH_BYTES = 64 << 20   # the library's static scratch array per device
 
 PA_F16, PA_BF16 = 0, 1
 _DTYPE_CODE = {torch.float16: PA_F16, torch.bfloat16: PA_BF16}
@@ -85,6 +88,8 @@ def _lib():
         P = ctypes.POINTER(_Args)
         lib.paged_attn_fwd.restype = ctypes.c_int
         lib.paged_attn_fwd.argtypes = [P, ctypes.c_void_p]
+        lib.paged_attn_fwd_noalloc.restype = ctypes.c_int
+        lib.paged_attn_fwd_noalloc.argtypes = [P, ctypes.c_void_p]
         lib.paged_kv_append.restype = ctypes.c_int
         lib.paged_kv_append.argtypes = [P, ctypes.c_void_p]
         lib.paged_attn_workspace_size.restype = ctypes.c_size_t
@@ -357,6 +362,30 @@ def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q
     if st != 0:
         raise PagedAttnError(st, "paged_attn_fwd")
     return out, softmax_lse
+
+
+def paged_attn_fwd_noalloc(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, *,
+                           out, softmax_lse, max_seqlen_q: int, max_seqlen_k: int = 0,
+                           k_new=None, v_new=None, causal: bool = False, num_splits: int = 0,
+                           softmax_scale=None, rotary_cos=None, rotary_sin=None,
+                           rotary_interleaved: bool = False, stream=None) -> None:
+    """The allocation-free entry point: as paged_attn_fwd, with the caller's
+    ``out`` / ``softmax_lse`` (required) and the library's static split-KV
+    scratch in place of a workspace; neither the binding nor the library
+    allocates anything, and a mixed batch runs as one launch.  Calls that
+    overlap on one GPU share the scratch and must be serialised."""
+    if out is None or softmax_lse is None:
+        raise ValueError("paged_attn_fwd_noalloc writes into the caller's out and softmax_lse")
+    args = make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q,
+                     max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, k_new=k_new,
+                     v_new=v_new, causal=causal, num_splits=num_splits,
+                     softmax_scale=softmax_scale, out=out, softmax_lse=softmax_lse,
+                     rotary_cos=rotary_cos, rotary_sin=rotary_sin,
+                     rotary_interleaved=rotary_interleaved)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = _lib().paged_attn_fwd_noalloc(ctypes.byref(args), ctypes.c_void_p(s.cuda_stream))
+    if st != 0:
+        raise PagedAttnError(st, "paged_attn_fwd_noalloc")
 
 
 def paged_kv_append(k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q, k_new, v_new, *,

@@ -12,10 +12,18 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 #include <vector>
 
 #include "paged_attn.h"
 #include "pa_kernels.h"
+
+// Device scratch of paged_attn_fwd_noalloc: the split-KV partials of calls
+// whose caller cannot allocate.  One array per device, held from the
+// library's load on that device until the process ends.  In host code its name
+// is only a stand-in: its device address comes from hipGetSymbolAddress.
+static constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -425,6 +433,33 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   return PA_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+pa_status scratch_address(void **out) {
+  static std::atomic<void *> addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return PA_ERR_UNSUPPORTED;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PA_ERR_HIP;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PA_OK;
+}
+
+template <class F>
+pa_status dispatch(const pa_fwd_args *a, F &&launch) {
+  const bool bf16 = a->dtype == PA_BF16;
+  if (a->head_dim == 128)
+    return bf16 ? launch(std::integral_constant<int, pa::kBF16>{}, std::integral_constant<int, 128>{})
+                : launch(std::integral_constant<int, pa::kF16>{}, std::integral_constant<int, 128>{});
+  return bf16 ? launch(std::integral_constant<int, pa::kBF16>{}, std::integral_constant<int, 64>{})
+              : launch(std::integral_constant<int, pa::kF16>{}, std::integral_constant<int, 64>{});
+}
+
 }  // namespace
 
 extern "C" {
@@ -489,12 +524,30 @@ pa_status paged_attn_fwd(const pa_fwd_args *args, void *stream) {
     return PA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipStream_t aux = static_cast<hipStream_t>(args->aux_stream);
-  const bool bf16 = args->dtype == PA_BF16;
-  if (args->head_dim == 128)
-    return bf16 ? launch_attention<pa::kBF16, 128>(args, pl, s, aux, true)
-                : launch_attention<pa::kF16, 128>(args, pl, s, aux, true);
-  return bf16 ? launch_attention<pa::kBF16, 64>(args, pl, s, aux, true)
-              : launch_attention<pa::kF16, 64>(args, pl, s, aux, true);
+  return dispatch(args, [&](auto dt, auto d) {
+    return launch_attention<decltype(dt)::value, decltype(d)::value>(args, pl, s, aux, true);
+  });
+}
+
+pa_status paged_attn_fwd_noalloc(const pa_fwd_args *args, void *stream) {
+  pa_status st = validate(args, false);
+  if (st != PA_OK) return st;
+  if (args->total_q == 0) return PA_OK;
+  const Plan pl = make_plan(args, device_cus());
+  if (pl.ws_bytes > kScratchBytes) return PA_ERR_SCRATCH;
+  pa_fwd_args a = *args;   // the caller's workspace and aux_stream are not used
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  a.aux_stream = nullptr;
+  if (pl.ws_bytes > 0) {
+    st = scratch_address(&a.workspace);
+    if (st != PA_OK) return st;
+    a.workspace_bytes = kScratchBytes;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dispatch(&a, [&](auto dt, auto d) {
+    return launch_attention<decltype(dt)::value, decltype(d)::value>(&a, pl, s, nullptr, false);
+  });
 }
 
 const char *paged_attn_status_string(int32_t status) {
@@ -508,6 +561,7 @@ const char *paged_attn_status_string(int32_t status) {
     case PA_ERR_HIP: return "a HIP launch or runtime call failed";
     case PA_ERR_ALIGN: return "a buffer moved in 16-byte vectors is not 16-byte aligned";
     case PA_ERR_PRECONDITION: return "device metadata breaks a precondition (PAGED_ATTN_DEBUG=1)";
+    case PA_ERR_SCRATCH: return "the call needs more split-KV scratch than paged_attn_fwd_noalloc's static 64 MiB array holds";
     default: return "unknown status";
   }
 }

@@ -123,7 +123,7 @@ def test_workspace_size_and_splits_for_are_host_only():
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         assert pa.paged_attn_status_string(code) != "unknown status"
     assert pa.paged_attn_status_string(99) == "unknown status"
 
@@ -174,3 +174,22 @@ def test_slabs_of_two_gib_or_more_are_rejected():
     a = valid_args(block_table=None, contig_alloc=1 << 20, num_heads_q=8, num_heads_kv=8,
                    head_dim=128)
     assert call_fwd(a) == 4
+
+
+def test_noalloc_entry_point_host_checks():
+    # the allocation-free entry point validates like paged_attn_fwd, ignores
+    # the workspace fields, and rejects a plan whose split-KV scratch exceeds
+    # its static 64 MiB array before anything is launched
+    f = pa._lib().paged_attn_fwd_noalloc
+    assert f(None, None) == 1
+    assert f(ctypes.byref(valid_args(head_dim=96)), None) == 4
+    assert f(ctypes.byref(valid_args(q=None)), None) == 1
+    big = valid_args(total_q=4096, max_seqlen_q=2048, num_splits=128)
+    need = pa.paged_attn_workspace_size(big)
+    assert need > pa.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), None) == pa.PA_ERR_SCRATCH
+    # a forced split whose partials fit would need a workspace in paged_attn_fwd,
+    # but is not refused for it here (it stops at no check: a decode batch of
+    # 2 rows with 4 splits is well within the array) - only sizes are compared
+    small = valid_args(num_splits=4)
+    assert 0 < pa.paged_attn_workspace_size(small) <= pa.NOALLOC_SCRATCH_BYTES
