@@ -152,7 +152,7 @@ def sweep(name, reps, out_path):
         print(json.dumps(rec), file=sys.stderr, flush=True)
 
     def make_call(case, inp, num_splits=None, max_seqlen_k=None, seqlens=None, append=None,
-                  rot=None):
+                  rot=None, aux=None):
         kn = inp.k_new if (append if append is not None else case.append) else None
         vn = inp.v_new if kn is not None else None
         seq = inp.cache_seqlens if seqlens is None else seqlens
@@ -174,7 +174,7 @@ def sweep(name, reps, out_path):
                               inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q,
                               max_seqlen_k=args.max_seqlen_k, k_new=kn, v_new=vn,
                               causal=case.causal, num_splits=args.num_splits, out=out,
-                              softmax_lse=lse, workspace=ws, **rk)
+                              softmax_lse=lse, workspace=ws, aux_stream=aux, **rk)
         return S, call
 
     def run(case, inp, **kw):
@@ -266,7 +266,9 @@ def sweep(name, reps, out_path):
                 c = wl.unified_varlen(nq, heads=heads, head_dim=hd)
                 inp = wl.make_inputs(c, "cuda")
                 S, med, mn = run(c, inp)
-                # the same call as one unified launch instead of two concurrent ones
+                # the other plans of a mixed batch: the two launches concurrent
+                # on two streams, and one unified launch
+                _, cmed, _ = run(c, inp, aux="auto")
                 os.environ["PAGED_ATTN_SINGLE_KERNEL"] = "1"
                 _, smed, _ = run(c, inp)
                 del os.environ["PAGED_ATTN_SINGLE_KERNEL"]
@@ -284,7 +286,8 @@ def sweep(name, reps, out_path):
                 dby = algorithmic_bytes(dec)
                 emit({"sweep": "unified", "nq": nq, "heads": heads, "head_dim": hd, "splits": S,
                       "ms": med, "ms_min": mn, "roofline_ms": t_roof, "frac": t_roof / med,
-                      "one_launch_ms": smed, "two_call_ms": dmed + pmed, "decode_only_ms": dmed,
+                      "concurrent_ms": cmed, "one_launch_ms": smed, "two_call_ms": dmed + pmed,
+                      "decode_only_ms": dmed,
                       "decode_only_frac": dby / (HBM_PEAK_GBS * 1e9) * 1e3 / dmed})
                 del inp, di, pi
                 torch.cuda.empty_cache()

@@ -170,7 +170,9 @@ typedef struct pa_fwd_args {
   /* Optional second stream (hipStream_t; NULL: none) for a batch that mixes
    * decode-mode and prefill-mode sequences: its decode units then run on it,
    * concurrently with the prefill units on the call's stream (see
-   * paged_attn_fwd).  Owned by the caller; the library only queues work on it. */
+   * paged_attn_fwd; measured faster than the one-stream plan only when the
+   * prefill part is large).  Owned by the caller; the library only queues
+   * work on it. */
   void *aux_stream;
 } pa_fwd_args;
 
@@ -181,16 +183,17 @@ typedef struct pa_fwd_args {
  * log-sum-exp combine.  Kernels run in that order; the call returns as soon
  * as they are queued.
  * A batch whose sizes allow both decode-mode sequences (q_len * group <= 16)
- * and prefill-mode ones, called with an aux_stream, runs its attention as two
- * concurrent launches: after the append on `stream`, an event forks
- * aux_stream off to run the decode units, the prefill units run on `stream`,
- * and `stream` then waits on a second event recorded on aux_stream before
- * the combine.  Work
- * queued on `stream` afterwards therefore sees the whole call, and a capture
- * of `stream` takes in both launches.  The two events are created for the
- * call and released once the join is queued.  Without an aux_stream (or with
- * the environment variable PAGED_ATTN_SINGLE_KERNEL=1) the attention is one
- * unified launch on `stream`; both plans give the same results, bit for bit.
+ * and prefill-mode ones runs its attention as two launches on `stream`: the
+ * prefill units (8-wave workgroups), then the decode units (4-wave
+ * workgroups).  Called with an aux_stream, the two run concurrently instead:
+ * after the append on `stream`, an event forks aux_stream off to run the
+ * decode units, the prefill units run on `stream`, and `stream` then waits on
+ * a second event recorded on aux_stream before the combine.  Work queued on
+ * `stream` afterwards therefore sees the whole call, and a capture of
+ * `stream` takes in both launches.  The two events are created for the call
+ * and released once the join is queued.  With the environment variable
+ * PAGED_ATTN_SINGLE_KERNEL=1 the attention is one unified launch on `stream`.
+ * Every plan gives the same results, bit for bit.
  * Returns PA_OK or the first host-detected error (nothing launched then);
  * PA_ERR_HIP if a launch or an event operation fails.
  */

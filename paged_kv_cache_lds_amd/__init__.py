@@ -315,7 +315,7 @@ def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q
                    causal: bool = False, num_splits: int = 0, softmax_scale=None, out=None,
                    softmax_lse=None, workspace=None, rotary_cos=None, rotary_sin=None,
                    rotary_interleaved: bool = False, stream=None,
-                   aux_stream="auto") -> Tuple[torch.Tensor, torch.Tensor]:
+                   aux_stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Paged attention forward (with optional in-call append of k_new/v_new).
 
     q [total_q, Hq, D]; k_cache/v_cache [num_pages, page_size, Hkv, D] (or
@@ -324,12 +324,12 @@ def paged_attn_fwd(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q
     ``max_seqlen_q`` must bound every q_len on the host side (no device read).
     ``rotary_cos`` / ``rotary_sin`` [rows, rotary_dim / 2] (element type) turn
     on the fused rotary embedding of q and k_new.
-    Everything is queued on ``stream`` (default: torch's current stream); a
-    batch that can mix decode-mode and prefill-mode sequences runs its decode
-    units on ``aux_stream`` (default "auto": the binding's own second stream
-    of the device; None: one launch on ``stream``), forked from ``stream`` and
-    joined back into it by the call, so later work on ``stream`` sees the whole
-    result.  Tensors the call allocates (out, softmax_lse, workspace when not
+    Everything is queued on ``stream`` (default: torch's current stream).  A
+    batch that can mix decode-mode and prefill-mode sequences runs its prefill
+    units and then its decode units there; with ``aux_stream`` (a stream, or
+    "auto" for the binding's own second stream of the device) the decode units
+    run on it instead, concurrently, forked from ``stream`` and joined back
+    into it by the call, so later work on ``stream`` sees the whole result.  Tensors the call allocates (out, softmax_lse, workspace when not
     given) are allocated on ``stream``, so the caching allocator does not hand
     them out again before the kernels queued there have finished.
     Returns (out [total_q, Hq, D], softmax_lse [total_q, Hq] fp32).

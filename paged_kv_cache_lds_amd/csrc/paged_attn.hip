@@ -326,14 +326,22 @@ pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode =
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-// A mixed batch (decode-mode and prefill-mode sequences) given a second
-// stream runs its attention as two concurrent launches: the decode units in
-// the decode-only kernel (four-wave workgroups, two per CU, longest first) on
-// the caller's aux_stream, the prefill units in the unified kernel on
-// `stream`.  An event recorded on `stream` after the append forks aux_stream
-// off, a second one recorded on aux_stream after its launch joins it back.
-// The events are created for the call and released right after the join is
-// queued (the runtime keeps them until they complete).
+// A mixed batch (decode-mode and prefill-mode sequences) runs its prefill
+// units in the unified kernel and then its decode units in the decode-only
+// kernel (four-wave workgroups, two per CU, longest first), both on `stream`.
+// Measured on one prefill chunk + 64 decode sequences (32 x 128 and 12 x 64,
+// chunks of 100 / 500 / 1000 tokens): faster than the same work as two calls
+// at every point, 2-8% faster than one unified launch (whose 8-wave
+// workgroups pair two decode units and hold the CU until the longer ends),
+// and faster than the two kernels on concurrent streams except at 12 x 64
+// with 500 / 1000-token chunks: a prefill workgroup needs a whole CU, and
+// while the decode launch keeps refilling the CUs it frees, the prefill
+// launch waits for CUs to drain.  Given a second stream (aux_stream) the
+// concurrent plan is used: an event recorded on `stream` after the append
+// forks aux_stream off for the decode units, a second one recorded on
+// aux_stream after its launch joins it back.  Those events are created for
+// the call and released right after the join is queued (the runtime keeps
+// them until they complete).
 struct Fork {
   hipEvent_t fork = nullptr, join = nullptr;
   ~Fork() {
@@ -387,8 +395,16 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   if (pl.all_decode) {
     hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(kThreads),
                        0, stream, p);
-  } else if (pl.may_mix && may_fork && aux != nullptr && aux != stream &&
-             !single_kernel_forced()) {
+  } else if (pl.may_mix && !single_kernel_forced() &&
+             !(may_fork && aux != nullptr && aux != stream)) {
+    p.unit_mode = 1;
+    hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid_pre),
+                       dim3(pa::kUThreads), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    p.unit_mode = 2;
+    hipLaunchKernelGGL((pa::attn_decode_kernel<DT, D>), dim3((unsigned)pl.grid_dec),
+                       dim3(kThreads), 0, stream, p);
+  } else if (pl.may_mix && !single_kernel_forced()) {
     Fork f;
     if (hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&f.join, hipEventDisableTiming) != hipSuccess ||

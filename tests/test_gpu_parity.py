@@ -224,9 +224,9 @@ def test_unified_varlen_with_prefix():
 
 
 # A batch that can mix decode-mode and prefill-mode sequences runs as two
-# concurrent launches when the call has a second stream (decode units on
-# aux_stream); without one (aux_stream=None), or with
-# PAGED_ATTN_SINGLE_KERNEL=1, it is one unified launch.  Both plans run the
+# launches on the call's stream (prefill units, then decode units); with a
+# second stream the two run concurrently (decode units on aux_stream); with
+# PAGED_ATTN_SINGLE_KERNEL=1 it is one unified launch.  Every plan runs the
 # same unit code, so they must agree bit for bit, and the one-launch plan
 # keeps its oracle parity.
 @pytest.mark.parametrize("nq,heads,hd", [(100, 32, 128), (1000, 12, 64)])
@@ -239,7 +239,7 @@ def test_unified_varlen_one_launch(nq, heads, hd, monkeypatch):
                                   wl.unified_varlen(100, heads=12, head_dim=64),
                                   wl.multi_token_decode(3, 700, 2)],
                          ids=lambda c: c.name)
-def test_two_launches_equal_one_launch(case):
+def test_mixed_batch_plans_agree(case, monkeypatch):
     if case.name.startswith("multi_token"):
         # one prefill-mode sequence among decode-mode ones
         case.q_lens = [2, 40, 2]
@@ -248,15 +248,21 @@ def test_two_launches_equal_one_launch(case):
     kc0, vc0 = inp.k_cache.clone(), inp.v_cache.clone()
     for s in (None, 2):
         got = {}
-        for plan in ("two", "one"):
+        for plan in ("sequential", "concurrent", "one"):
             inp.k_cache.copy_(kc0)
             inp.v_cache.copy_(vc0)
-            out, lse = gpu_call(inp, num_splits=s, aux_stream="auto" if plan == "two" else None)
+            if plan == "one":
+                monkeypatch.setenv("PAGED_ATTN_SINGLE_KERNEL", "1")
+            out, lse = gpu_call(inp, num_splits=s,
+                                aux_stream="auto" if plan == "concurrent" else None)
+            monkeypatch.delenv("PAGED_ATTN_SINGLE_KERNEL", raising=False)
             got[plan] = (out.clone(), lse.clone(), inp.k_cache.clone(), inp.v_cache.clone())
-        for name, a, b in zip(("out", "lse", "k_cache", "v_cache"), got["two"], got["one"]):
-            bits = torch.int16 if a.element_size() == 2 else torch.int32
-            assert torch.equal(a.view(bits), b.view(bits)), \
-                f"{case.name} S={s}: {name} differs between the plans"
+        for other in ("concurrent", "one"):
+            for name, a, b in zip(("out", "lse", "k_cache", "v_cache"), got["sequential"],
+                                  got[other]):
+                bits = torch.int16 if a.element_size() == 2 else torch.int32
+                assert torch.equal(a.view(bits), b.view(bits)), \
+                    f"{case.name} S={s}: {name} differs between the sequential and {other} plans"
 
 
 # ---------------------------------------------------------------------------
@@ -489,10 +495,13 @@ def test_every_tail_position_of_a_tile(P):
     run_parity(c2, splits=(1, None))
 
 
-def test_mixed_batch_on_a_user_stream():
-    # a mixed batch queued on a stream of the caller's: work queued on that
-    # stream right after the call (no synchronisation) sees the whole result,
-    # which equals the same call on the default stream bit for bit
+@pytest.mark.parametrize("aux", [None, "auto"])
+def test_mixed_batch_on_a_user_stream(aux):
+    # a mixed batch queued on a stream of the caller's (both plans: two
+    # launches on that stream, or forked onto a second one and joined back):
+    # work queued on that stream right after the call (no synchronisation)
+    # sees the whole result, which equals the same call on the default stream
+    # bit for bit
     c = wl.unified_varlen(100, heads=8, head_dim=128)
     say(f"case {c.name} seed {c.seed} on a user stream")
     inp = make_inputs(c, "cuda")
@@ -507,7 +516,7 @@ def test_mixed_batch_on_a_user_stream():
         out, lse = pa.paged_attn_fwd(
             inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens, inp.cu_seqlens_q,
             max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=inp.max_seqlen_k, k_new=inp.k_new,
-            v_new=inp.v_new, causal=c.causal, stream=s)
+            v_new=inp.v_new, causal=c.causal, stream=s, aux_stream=aux)
         out_copy, lse_copy = out.clone(), lse.clone()
         kc_copy, vc_copy = inp.k_cache.clone(), inp.v_cache.clone()
     torch.cuda.synchronize()
