@@ -210,9 +210,18 @@ def sweep(name, reps, out_path):
                                     pages_of=[])
                     S, med, mn = run(c, sub)
                     by = algorithmic_bytes(c)
-                    emit({"sweep": "decode", "P": P, "batch": B, "ctx": ctx, "splits": S,
-                          "ms": med, "ms_min": mn, "GBps": by / med / 1e6,
-                          "frac": by / med / 1e6 / HBM_PEAK_GBS})
+                    rec = {"sweep": "decode", "P": P, "batch": B, "ctx": ctx, "splits": S,
+                           "ms": med, "ms_min": mn, "GBps": by / med / 1e6,
+                           "frac": by / med / 1e6 / HBM_PEAK_GBS}
+                    if P == 16:
+                        # forced split budgets beside the heuristic's
+                        forced = {}
+                        for fs in (1, 2, 4, 8):
+                            forced[fs] = med if fs == S else run(c, sub, num_splits=fs)[1]
+                        best = min(forced, key=forced.get)
+                        rec.update({"forced_ms": forced, "best_splits": best,
+                                    "heuristic_over_best": med / min(med, forced[best])})
+                    emit(rec)
             del inp
             torch.cuda.empty_cache()
     elif name == "gqa":

@@ -484,12 +484,15 @@ int32_t paged_attn_num_splits(int32_t batch, int32_t total_q, int32_t num_heads_
                               int32_t num_heads_kv, int32_t head_dim, int32_t max_seqlen_q,
                               int32_t max_seqlen_k, int32_t num_cus) {
   // Host-only cost model (no device length is read).  Work units without any
-  // split: one per (sequence, kv head) plus the prefill tiles.  If they cover
-  // the machine twice over (two resident 4-wave workgroups per compute unit)
-  // splitting only adds partial-result traffic.  Otherwise split each key
-  // range so the units reach that count, but keep at least 8 key tiles of
-  // 32 per split (two per wave) so a split's fixed cost stays amortised, and
-  // stay within the cap of 128.
+  // split: one per (sequence, kv head) plus the prefill tiles.  Once they give
+  // every compute unit a workgroup, splitting only adds partial-result
+  // traffic and a combine.  Otherwise split each key range so the units reach
+  // one per compute unit, but keep at least 8 key tiles of 32 per split (two
+  // per wave) so a split's fixed cost stays amortised, and stay within the
+  // cap of 128.  (Measured over MHA decode, 32 x 128, batch 1-256 x context
+  // 512-4096: with this target the chosen budget is the fastest of 1/2/4/8 or
+  // within a few percent of it at every point; targeting two workgroups per
+  // compute unit split 256-unit batches and made them up to 19% slower.)
   (void)head_dim;
   if (batch < 1 || num_heads_q < 1 || num_heads_kv < 1 || max_seqlen_k < 1) return 1;
   if (num_cus < 1) num_cus = 256;
@@ -497,7 +500,7 @@ int32_t paged_attn_num_splits(int32_t batch, int32_t total_q, int32_t num_heads_
   long units = (long)batch * num_heads_kv;
   if ((long)max_seqlen_q * group > pa::kDecodeRows && total_q > 0)
     units += cdiv((long)total_q * group, pa::kPrefillRows) * num_heads_kv;
-  const long target = 2L * num_cus;
+  const long target = num_cus;
   if (units >= target) return 1;
   long s = cdiv(target, units);
   const long tiles = cdiv(max_seqlen_k, pa::kKeyTile);
