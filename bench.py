@@ -264,18 +264,9 @@ def sweep(name, reps, out_path):
             c = wl.causal_prefill_append(nq, prefix)
             inp = wl.make_inputs(c, "cuda")
             S, med, mn = run(c, inp)
-            # the same call with every row appended by the append kernel first
-            os.environ["PAGED_ATTN_SEPARATE_APPEND"] = "1"
-            _, smed, _ = run(c, inp)
-            del os.environ["PAGED_ATTN_SEPARATE_APPEND"]
-            # attention alone on the same keys (rows already in the pages)
-            seq_after = inp.cache_seqlens + c.q_lens[0]
-            _, amed, _ = run(c, inp, seqlens=seq_after, append=False)
             fl = causal_flops(c)
             emit({"sweep": "prefill", "nq": nq, "prefix": prefix, "ms": med, "ms_min": mn,
-                  "TFLOPs": fl / med / 1e9, "frac": fl / med / 1e9 / MFMA_F16_PEAK_TFS,
-                  "separate_append_ms": smed, "attention_only_ms": amed,
-                  "attention_only_frac": fl / amed / 1e9 / MFMA_F16_PEAK_TFS})
+                  "TFLOPs": fl / med / 1e9, "frac": fl / med / 1e9 / MFMA_F16_PEAK_TFS})
             del inp
             torch.cuda.empty_cache()
     elif name == "unified":

@@ -39,14 +39,7 @@ struct FwdParams {
   Rotary rot;          // rotary embedding of q (rot.cos == nullptr: none)
   long q_stride;       // elements between consecutive tokens' q rows
   int unit_mode;       // 0: every unit; 1: prefill units only; 2: decode units only
-                       // (a mixed batch split over two launches)
-  // Fused append (batches of prefill-mode sequences only): the units of a
-  // sequence with an empty cache read every key from k_new / v_new (dense
-  // [total_q, hkv, D]) and each copies its own tokens' new rows into the pool;
-  // the append kernel appends the other sequences beforehand.
-  const uint16_t *k_new;
-  const uint16_t *v_new;
-  int fused_append;
+                       // (a mixed batch split over two concurrent launches)
 };
 
 struct AppendParams {
@@ -62,7 +55,6 @@ struct AppendParams {
                        // (q_len * group <= kDecodeRows)
   Rotary rot;          // rotary embedding of the new keys (rot.cos == nullptr: none)
   long kn_stride, vn_stride;   // elements between consecutive tokens' k_new / v_new rows
-  int skip_empty;      // skip sequences with an empty cache (a fused append's)
 };
 
 // ---------------------------------------------------------------------------
@@ -78,14 +70,13 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
   const int b = blockIdx.y;
   const int cu_b = p.cu_seqlens_q[b];
   // rows past total_q (malformed cu_seqlens_q) are never touched
-  const int q_len_b = max(0, min(p.cu_seqlens_q[b + 1], p.total_q) - cu_b);
-  const int L = p.cache_seqlens[b];
-  const int q_len = p.skip_empty && L <= 0 ? 0 : q_len_b;
+  const int q_len = max(0, min(p.cu_seqlens_q[b + 1], p.total_q) - cu_b);
   const int tok0 = blockIdx.x * p.tokens_per_block;
   if (tok0 >= q_len) return;
-  if (p.seq_mode != 0 && (p.seq_mode == 2) != (q_len_b * p.group <= kDecodeRows)) return;
+  if (p.seq_mode != 0 && (p.seq_mode == 2) != (q_len * p.group <= kDecodeRows)) return;
   const int ntok = min(p.tokens_per_block, q_len - tok0);
   const int vec_per_row = p.hkv * p.head_dim / 8;   // 16-byte vectors per token row
+  const int L = p.cache_seqlens[b];
   const int work = ntok * vec_per_row * 2;
   for (int idx = threadIdx.x; idx < work; idx += kThreads) {
     const int which = idx / (ntok * vec_per_row);     // 0: K, 1: V

@@ -129,14 +129,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
                                    sm_m + kWaves, sm_l + kWaves);
     } else {
       const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
-      // a fused append's sequence with an empty cache: every key is a new row
-      const bool fresh = p.fused_append && si.K_b == si.q_len;
-      if (fresh)
-        prefill_unit<DT, D, false, true>(p, u.b, g, n_qt - 1 - u.off, si, pool);
-      else if (p.geom.table != nullptr)
-        prefill_unit<DT, D, true, false>(p, u.b, g, n_qt - 1 - u.off, si, pool);
+      if (p.geom.table != nullptr)
+        prefill_unit<DT, D, true>(p, u.b, g, n_qt - 1 - u.off, si, pool);
       else
-        prefill_unit<DT, D, false, false>(p, u.b, g, n_qt - 1 - u.off, si, pool);
+        prefill_unit<DT, D, false>(p, u.b, g, n_qt - 1 - u.off, si, pool);
     }
   }
 }

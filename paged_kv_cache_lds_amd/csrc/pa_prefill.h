@@ -40,12 +40,7 @@ namespace pa {
 constexpr float kRescaleThreshold = 8.f;   // log2 units
 constexpr float kSumBound = 16384.f;       // 2^14
 
-// kFresh: a unit of a sequence with an empty cache under a fused append (all
-// its keys are new rows of this call): every tile comes from the sequence's
-// rows of k_new / v_new, and the unit copies its own tokens' rows into the
-// pool.  A separate instantiation, so the path that reads the pool keeps its
-// register allocation.
-template <int DT, int D, bool kPaged, bool kFresh>
+template <int DT, int D, bool kPaged>
 __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, const int g,
                                              const int qtile, const SeqInfo si,
                                              const LdsPool &pool) {
@@ -120,7 +115,7 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   const int shift = cg.page_shift;
   const uint32_t row_bytes = (uint32_t)p.hkv * D * 2;
   const uint32_t slab_bytes = paged ? row_bytes << shift : (uint32_t)cg.contig_alloc * row_bytes;
-  const int limit = (paged || kFresh) ? wg_bound : min(wg_bound, cg.contig_alloc);
+  const int limit = paged ? wg_bound : min(wg_bound, cg.contig_alloc);
   const int lrow = lane / CPR;
   const int pch = lane % CPR;
   const int kx = D == 128 ? ((4 * (bb & 1) + lrow) & 7) : ((4 * bb + (lrow >> 1)) & 7);
@@ -143,9 +138,7 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     last_pg = max(0, min(cg.mpp, (wg_bound + (1 << shift) - 1) >> shift) - 1);
   }
   auto load_id = [&](int t) -> int {
-    if constexpr (kFresh)
-      return 0;   // unused: a fresh unit's tiles are not in the pool
-    else if constexpr (kPaged)
+    if constexpr (kPaged)
       return trow[min((t * kPTile + bb * RPB) >> shift, last_pg)];
     else
       return b;
@@ -157,38 +150,24 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   // row inside the page (capped at the slab size so that an out-of-range lane
   // offset cannot wrap back into range).
   const uint32_t pmask = paged ? (1u << shift) - 1u : 0xffffffffu;
-  // A fresh unit's tile t is the sequence's new rows 32 t .. 32 t + 31 in
-  // k_new / v_new (dense like the pool's rows): the "slab" of the descriptor
-  // starts at the tile's first row; lanes past the unit's bound read zeros
-  // through kOOB as in the pool path.
-  const uint16_t *const k_src = kFresh ? p.k_new + (long)si.cu_b * p.hkv * D : p.k_cache;
-  const uint16_t *const v_src = kFresh ? p.v_new + (long)si.cu_b * p.hkv * D : p.v_cache;
   struct TileInfo {
     uint32_t off_lo, off_hi, nrec, uni;
   };
   auto tile_info = [&](int t, int id) -> TileInfo {
+    const uint32_t pg = (uint32_t)id;
+    const uint64_t off = (uint64_t)pg * slab_bytes;
     TileInfo ti;
-    if constexpr (kFresh) {
-      const uint64_t off = (uint64_t)(t * kPTile) * row_bytes;
-      ti.off_lo = (uint32_t)off;
-      ti.off_hi = (uint32_t)(off >> 32);
-      ti.nrec = (uint32_t)kPTile * row_bytes;
-      ti.uni = (uint32_t)(bb * RPB) * row_bytes;
-    } else {
-      const uint32_t pg = (uint32_t)id;
-      const uint64_t off = (uint64_t)pg * slab_bytes;
-      ti.off_lo = (uint32_t)off;
-      ti.off_hi = (uint32_t)(off >> 32);
-      ti.nrec = (!paged || pg < (uint32_t)cg.num_pages) ? slab_bytes : 0u;
-      ti.uni = min(((uint32_t)(t * kPTile + bb * RPB) & pmask) * row_bytes, slab_bytes);
-    }
+    ti.off_lo = (uint32_t)off;
+    ti.off_hi = (uint32_t)(off >> 32);
+    ti.nrec = (!paged || pg < (uint32_t)cg.num_pages) ? slab_bytes : 0u;
+    ti.uni = min(((uint32_t)(t * kPTile + bb * RPB) & pmask) * row_bytes, slab_bytes);
     return ti;
   };
   // this wave's block of one matrix (K or V) of tile t into an LDS slot
-  auto load_block = [&](const uint16_t *src, uint16_t *slot, uint32_t lane_part, int blk, int t,
+  auto load_block = [&](const uint16_t *cache, uint16_t *slot, uint32_t lane_part, int blk, int t,
                         const TileInfo &ti) {
     const uint16_t *base =
-        (const uint16_t *)((uintptr_t)src + (((uint64_t)ti.off_hi << 32) | ti.off_lo));
+        (const uint16_t *)((uintptr_t)cache + (((uint64_t)ti.off_hi << 32) | ti.off_lo));
     const bool ok = t * kPTile + bb * RPB + lrow < limit;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(base, ti.nrec), (lds_void *)(slot + blk), 16,
                                              ok ? lane_part : kOOB, ti.uni, 0, 0);
@@ -426,51 +405,16 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     ti_v = tile_info(3, load_id(3));
     id_k = load_id(4);
     if (loader) {
-      load_block(k_src, k_slot[0], k_lane, k_blk, 0, ti_0);
-      load_block(v_src, v_slot[0], v_lane, v_blk, 0, ti_0);
-      load_block(k_src, k_slot[1], k_lane, k_blk, 1, ti_1);
-      load_block(v_src, v_slot[1], v_lane, v_blk, 1, ti_1);
-      load_block(k_src, k_slot[2], k_lane, k_blk, 2, ti_2);
-      load_block(v_src, v_slot[2], v_lane, v_blk, 2, ti_2);
-      load_block(k_src, k_slot[3], k_lane, k_blk, 3, ti_v);
-    }
-  }
-  // Fused append: the unit copies the new K and V rows (kv head g) of its own
-  // tokens - those whose first packed row is one of its rows - into the pool.
-  // Two threads per token, half a row each.  The loads go out with the first
-  // tiles' and the stores after the prologue's first wait; the second wait
-  // covers the stores, so the main loop's counted waits see tile loads only.
-  // No unit reads these pool rows in this call (its tiles come from k_new /
-  // v_new).
-  constexpr int CH2 = D / 16;   // 16-byte chunks per thread and matrix
-  u32x4 cp_k[CH2], cp_v[CH2];
-  long cp_dst = -1;             // element offset of the thread's half row in the pool
-  if constexpr (kFresh) {
-    const int tok_lo = (wg_row0 + group - 1) / group;
-    const int tok_hi = min((wg_row0 + wg_rows + group - 1) / group, si.q_len);
-    const int tk = tok_lo + (tid >> 1);
-    if (tk < tok_hi) {
-      const int c0 = (tid & 1) * CH2 * 8;
-      const long src = (long)(si.cu_b + tk) * (p.hkv * D) + g * D + c0;
-#pragma unroll
-      for (int c = 0; c < CH2; ++c) {
-        cp_k[c] = load16(p.k_new + src + c * 8);
-        cp_v[c] = load16(p.v_new + src + c * 8);
-      }
-      const long prow = physical_row(cg, b, tk);   // the cache is empty: position tk
-      cp_dst = prow < 0 ? -1L : prow * (p.hkv * D) + g * D + c0;
+      load_block(p.k_cache, k_slot[0], k_lane, k_blk, 0, ti_0);
+      load_block(p.v_cache, v_slot[0], v_lane, v_blk, 0, ti_0);
+      load_block(p.k_cache, k_slot[1], k_lane, k_blk, 1, ti_1);
+      load_block(p.v_cache, v_slot[1], v_lane, v_blk, 1, ti_1);
+      load_block(p.k_cache, k_slot[2], k_lane, k_blk, 2, ti_2);
+      load_block(p.v_cache, v_slot[2], v_lane, v_blk, 2, ti_2);
+      load_block(p.k_cache, k_slot[3], k_lane, k_blk, 3, ti_v);
     }
   }
   wait_then_barrier<0>();
-  if (cp_dst >= 0) {
-    uint16_t *kd = const_cast<uint16_t *>(p.k_cache) + cp_dst;
-    uint16_t *vd = const_cast<uint16_t *>(p.v_cache) + cp_dst;
-#pragma unroll
-    for (int c = 0; c < CH2; ++c) {
-      store16(kd + c * 8, cp_k[c]);
-      store16(vd + c * 8, cp_v[c]);
-    }
-  }
   if (rot_q) rot_apply_split<DT, QS>(p.rot, rot_pos, hh, qf, rot_c, rot_s);
   {
     f32x16 s0;
@@ -500,8 +444,8 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     auto issue_loads = [&]() {
       ti_k = tile_info(t + 4, id_k);
       if (loader) {
-        load_block(k_src, k_slot[ph], k_lane, k_blk, t + 4, ti_k);
-        load_block(v_src, v_slot[(ph + 3) & 3], v_lane, v_blk, t + 3, ti_v);
+        load_block(p.k_cache, k_slot[ph], k_lane, k_blk, t + 4, ti_k);
+        load_block(p.v_cache, v_slot[(ph + 3) & 3], v_lane, v_blk, t + 3, ti_v);
       }
     };
     if (grp_b) issue_loads();

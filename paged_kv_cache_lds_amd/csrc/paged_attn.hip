@@ -271,12 +271,6 @@ bool single_kernel_forced() {
   return e != nullptr && std::strcmp(e, "1") == 0;
 }
 
-// PAGED_ATTN_SEPARATE_APPEND=1: always append with the append kernel alone
-bool separate_append_forced() {
-  const char *e = std::getenv("PAGED_ATTN_SEPARATE_APPEND");
-  return e != nullptr && std::strcmp(e, "1") == 0;
-}
-
 pa::Rotary rotary_of(const pa_fwd_args *a) {
   pa::Rotary r;
   r.cos = static_cast<const uint16_t *>(a->rotary_cos);
@@ -298,10 +292,8 @@ pa::CacheGeom geom_of(const pa_fwd_args *a) {
 }
 
 // seq_mode: 0 every sequence, 1 prefill-mode sequences only, 2 decode-mode
-// sequences only.  skip_empty: leave sequences with an empty cache alone (a
-// fused append copies their rows).
-pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode = 0,
-                        bool skip_empty = false) {
+// sequences only
+pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode = 0) {
   if (a->total_q == 0 || a->max_seqlen_q == 0) return PA_OK;
   pa::AppendParams p;
   p.k_cache = static_cast<uint16_t *>(a->k_cache);
@@ -323,7 +315,6 @@ pa_status launch_append(const pa_fwd_args *a, hipStream_t stream, int seq_mode =
   p.tokens_per_block = std::max(1, 1024 / (2 * vec_per_row));
   p.seq_mode = seq_mode;
   p.group = a->num_heads_q / a->num_heads_kv;
-  p.skip_empty = skip_empty;
   const int rows = seq_mode == 2 ? std::min(a->max_seqlen_q, std::max(1, pa::kDecodeRows / p.group))
                                  : a->max_seqlen_q;
   dim3 grid((unsigned)cdiv(rows, p.tokens_per_block), (unsigned)a->batch);
@@ -393,21 +384,12 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   p.all_decode = pl.all_decode;
   p.rot = rotary_of(a);
   p.unit_mode = 0;
-  // Fused append: when every sequence is prefill-mode (no decode unit can
-  // exist), with dense new rows and no rotary embedding, the units of a
-  // sequence with an empty cache read its keys from k_new / v_new and copy
-  // them into the pool themselves; the append kernel appends the others.
-  p.fused_append = a->k_new != nullptr && !pl.all_decode && !pl.may_mix &&
-                   a->rotary_cos == nullptr && a->k_new_row_stride == 0 &&
-                   a->v_new_row_stride == 0 && !separate_append_forced();
-  p.k_new = p.fused_append ? static_cast<const uint16_t *>(a->k_new) : nullptr;
-  p.v_new = p.fused_append ? static_cast<const uint16_t *>(a->v_new) : nullptr;
   if (pl.grid > 0x7fffffffL || pl.grid_dec > 0x7fffffffL || pl.grid_pre > 0x7fffffffL)
     return PA_ERR_SHAPE;
-  // every row the attention reads from the pool is appended before any
-  // attention launch, on either stream
+  // every row is appended before any attention launch, on either stream,
+  // reads the pages
   if (a->k_new != nullptr) {
-    const pa_status st = launch_append(a, stream, 0, p.fused_append != 0);
+    const pa_status st = launch_append(a, stream);
     if (st != PA_OK) return st;
   }
   if (pl.all_decode) {

@@ -561,48 +561,3 @@ def test_allocations_follow_the_call_stream():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "out differs"
     assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), "lse differs"
-
-
-# Batches of prefill-mode sequences with k_new append the rows of sequences
-# with an empty cache inside the attention kernel (each prefill unit copies
-# its own tokens' rows; the units read those keys straight from k_new /
-# v_new), and the rest with the append kernel.  PAGED_ATTN_SEPARATE_APPEND=1
-# appends everything with the append kernel first; both must agree bit for
-# bit, pools included.
-FUSED_CASES = [
-    Case(name="fused_mha_empty", q_lens=[600, 300, 257], cache_seqlens=[0, 0, 0], num_heads_q=8,
-         num_heads_kv=8, head_dim=128, dtype="f16", page_size=16, append=True, causal=True,
-         seed=7401),
-    Case(name="fused_mixed_prefix", q_lens=[300, 400, 64, 129], cache_seqlens=[0, 77, 0, 513],
-         num_heads_q=8, num_heads_kv=4, head_dim=128, dtype="bf16", page_size=32, append=True,
-         causal=True, seed=7402),
-    Case(name="fused_gqa3_d64", q_lens=[500, 97], cache_seqlens=[0, 0], num_heads_q=12,
-         num_heads_kv=4, head_dim=64, dtype="f16", page_size=256, append=True, causal=True,
-         seed=7403),
-    Case(name="fused_contiguous", q_lens=[333, 290], cache_seqlens=[0, 15], num_heads_q=4,
-         num_heads_kv=2, head_dim=128, dtype="f16", page_size=None, contig_alloc=1024,
-         append=True, causal=True, seed=7404),
-    Case(name="fused_non_causal", q_lens=[200, 200], cache_seqlens=[0, 0], num_heads_q=4,
-         num_heads_kv=4, head_dim=64, dtype="bf16", page_size=16, append=True, causal=False,
-         seed=7405),
-]
-
-
-@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: c.name)
-def test_fused_append_equals_separate_append(case, monkeypatch):
-    say(f"case {case.name} seed {case.seed}: fused vs separate append")
-    run_parity(case)                 # the default (fused) path against the oracle
-    inp = make_inputs(case, "cuda")
-    kc0, vc0 = inp.k_cache.clone(), inp.v_cache.clone()
-    got = {}
-    for mode in ("fused", "separate"):
-        inp.k_cache.copy_(kc0)
-        inp.v_cache.copy_(vc0)
-        if mode == "separate":
-            monkeypatch.setenv("PAGED_ATTN_SEPARATE_APPEND", "1")
-        out, lse = gpu_call(inp)
-        monkeypatch.delenv("PAGED_ATTN_SEPARATE_APPEND", raising=False)
-        got[mode] = (out.clone(), lse.clone(), inp.k_cache.clone(), inp.v_cache.clone())
-    for name, a, b in zip(("out", "lse", "k_cache", "v_cache"), got["fused"], got["separate"]):
-        bits = torch.int16 if a.element_size() == 2 else torch.int32
-        assert torch.equal(a.view(bits), b.view(bits)), f"{case.name}: {name} differs"
