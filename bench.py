@@ -264,9 +264,14 @@ def sweep(name, reps, out_path):
             c = wl.causal_prefill_append(nq, prefix)
             inp = wl.make_inputs(c, "cuda")
             S, med, mn = run(c, inp)
+            # attention alone on the same keys (the rows are in the pages by now)
+            seq_after = inp.cache_seqlens + c.q_lens[0]
+            _, amed, _ = run(c, inp, seqlens=seq_after, append=False)
             fl = causal_flops(c)
             emit({"sweep": "prefill", "nq": nq, "prefix": prefix, "ms": med, "ms_min": mn,
-                  "TFLOPs": fl / med / 1e9, "frac": fl / med / 1e9 / MFMA_F16_PEAK_TFS})
+                  "TFLOPs": fl / med / 1e9, "frac": fl / med / 1e9 / MFMA_F16_PEAK_TFS,
+                  "attention_only_ms": amed,
+                  "attention_only_frac": fl / amed / 1e9 / MFMA_F16_PEAK_TFS})
             del inp
             torch.cuda.empty_cache()
     elif name == "unified":
