@@ -14,7 +14,10 @@
 
 namespace pa {
 
-template <int DT, int D, bool kUnified>
+// NH: kv heads per decode unit in the decode-only kernel (1, or 2 for a pair
+// of adjacent heads, see decode_unit_pair); workgroups number units per
+// group of NH kv heads.
+template <int DT, int D, bool kUnified, int NH = 1>
 __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   constexpr int NW = kUnified ? kUWaves : kWaves;   // waves of the workgroup
   __shared__ float sm_m[NW][kDecodeRows];           // per-wave decode states (two halves
@@ -22,8 +25,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   __shared__ int s_wsum[NW];
   __shared__ int s_found[2 * kFound];
 
-  const int g = blockIdx.x % p.hkv;
-  const int wg = blockIdx.x / p.hkv;
+  static_assert(NH == 1 || !kUnified, "pairs of heads only in the decode-only kernel");
+  const int hgroups = p.hkv / NH;
+  const int g = blockIdx.x % hgroups;   // kv head (NH = 1) or pair of kv heads (NH = 2)
+  const int wg = blockIdx.x / hgroups;
   UnitInfo u;
   bool decode = true;
   bool have = true;
@@ -79,8 +84,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   if constexpr (!kUnified) {
     // decode-only kernel: one contiguous array, a K and a V tile per wave
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kWaves * 2 * kKeyTile * D];
-    decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si, ContigDecodeLds<kKeyTile * D>{lds},
-                               sm_m, sm_l);
+    if constexpr (NH == 2)
+      decode_unit_pair<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si,
+                                      ContigDecodeLds<kKeyTile * D>{lds}, sm_m, sm_l);
+    else
+      decode_unit<DT, D, kWaves>(p, u.b, g, u.off, u.splits, si,
+                                 ContigDecodeLds<kKeyTile * D>{lds}, sm_m, sm_l);
   } else {
     // unified kernel: sixteen separate 32-row slots - a K/V pair per wave of a
     // decode unit, four K and four V slots of a prefill unit (K slots at
@@ -140,10 +149,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
 // Decode-only batches (every sequence fits a decode unit, known on the host),
 // and the decode units of a mixed batch launched beside its prefill units:
 // four waves, two workgroups per CU.
-template <int DT, int D>
+template <int DT, int D, int NH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_decode_kernel(FwdParams p) {
-  attn_fwd_body<DT, D, false>(p);
+  attn_fwd_body<DT, D, false, NH>(p);
 }
 
 // Unified kernel for any mix of prefill and decode sequences: eight waves,

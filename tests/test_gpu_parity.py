@@ -390,7 +390,7 @@ def test_varlen_equals_one_call_per_sequence():
 
 
 @pytest.mark.parametrize("batch", [40, 1024, 1030])
-def test_decode_varlen_unit_order(batch):
+def test_decode_varlen_unit_order(batch, monkeypatch):
     # decode-only batches with one unit per sequence run their units longest
     # first (up to 1024 sequences; index order past that): unsorted lengths
     # with ties and (0, 0) padding slots; results must not depend on the order
@@ -404,10 +404,29 @@ def test_decode_varlen_unit_order(batch):
              num_heads_q=8, num_heads_kv=2, head_dim=64, dtype="f16", page_size=16, append=True,
              causal=True, seed=5200 + batch)
     inp, _ = run_parity(c, splits=(1,))
-    # bit-exact against calls over a few single sequences
     kc_after, vc_after = inp.k_cache.clone(), inp.v_cache.clone()
     cu = inp.cu_seqlens_q.cpu().tolist()
     seq_after = (inp.cache_seqlens + torch.tensor(q_lens, dtype=torch.int32, device="cuda")).contiguous()
+
+    def whole(order):
+        """The batch with its sequences in `order` (a permutation): per-sequence results."""
+        q = torch.cat([inp.q[cu[b]:cu[b + 1]] for b in order])
+        cu_o = torch.tensor(np.concatenate([[0], np.cumsum([q_lens[b] for b in order])]),
+                            dtype=torch.int32, device="cuda")
+        o, l = pa.paged_attn_fwd(q, kc_after, vc_after, inp.block_table[order].contiguous(),
+                                 seq_after[order].contiguous(), cu_o, max_seqlen_q=1, causal=True,
+                                 num_splits=1)
+        torch.cuda.synchronize()
+        cu_h = cu_o.cpu().tolist()
+        return {b: (o[cu_h[i]:cu_h[i + 1]], l[cu_h[i]:cu_h[i + 1]]) for i, b in enumerate(order)}
+
+    # the batch in reverse order runs its units in another order (and, at 1024
+    # sequences and more x 2 kv heads, as pair units): the same bits
+    fwd, rev = whole(list(range(batch))), whole(list(range(batch))[::-1])
+    for b in range(batch):
+        assert torch.equal(fwd[b][0], rev[b][0]) and torch.equal(fwd[b][1], rev[b][1]), f"seq {b}"
+    # bit-exact against calls over a few single sequences, one-head units in both
+    monkeypatch.setenv("PAGED_ATTN_HEAD_PAIRS", "0")
     full_out, full_lse = pa.paged_attn_fwd(inp.q, kc_after, vc_after, inp.block_table, seq_after,
                                            inp.cu_seqlens_q, max_seqlen_q=1, causal=True, num_splits=1)
     torch.cuda.synchronize()
@@ -561,3 +580,36 @@ def test_allocations_follow_the_call_stream():
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "out differs"
     assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), "lse differs"
+
+
+# All-decode batches large enough to give every compute unit two units of a
+# pair of kv heads run decode units over pairs of adjacent kv heads (one load
+# fetches both heads' slices of a key's row); PAGED_ATTN_HEAD_PAIRS=0 keeps
+# one-head units.  Both against the oracle, and within a few output ulps of
+# each other (different tile sizes and MFMA shapes round differently).
+PAIR_CASES = [
+    Case(name="pairs_mha_f16", q_lens=[1] * 64, cache_seqlens=[37 + 11 * i for i in range(64)],
+         num_heads_q=16, num_heads_kv=16, head_dim=128, dtype="f16", page_size=16, append=True,
+         causal=True, seed=7501),
+    Case(name="pairs_gqa8_bf16", q_lens=[1] * 80, cache_seqlens=[300 - 3 * i for i in range(80)],
+         num_heads_q=112, num_heads_kv=14, head_dim=128, dtype="bf16", page_size=32,
+         causal=True, seed=7502),
+    Case(name="pairs_q2_g2_d64", q_lens=[2] * 70, cache_seqlens=[90 + (7 * i) % 50 for i in range(70)],
+         num_heads_q=32, num_heads_kv=16, head_dim=64, dtype="f16", page_size=256, append=True,
+         causal=True, seed=7503),
+    Case(name="pairs_contiguous_bf16", q_lens=[1] * 66, cache_seqlens=[5 + 9 * i for i in range(66)],
+         num_heads_q=16, num_heads_kv=16, head_dim=128, dtype="bf16", page_size=None,
+         contig_alloc=640, causal=False, seed=7504),
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=lambda c: c.name)
+def test_decode_units_over_head_pairs(case, monkeypatch):
+    # batch x kv heads >= 4 x 256 compute units: pair units
+    assert case.batch * case.num_heads_kv >= 1024
+    inp, errs = run_parity(case, splits=(None, 3))
+    say(f"  pair units: max out err {max(errs):.3g}")
+    monkeypatch.setenv("PAGED_ATTN_HEAD_PAIRS", "0")
+    inp1, errs1 = run_parity(case, splits=(None,))
+    monkeypatch.delenv("PAGED_ATTN_HEAD_PAIRS")
+    say(f"  one-head units: max out err {max(errs1):.3g}")
