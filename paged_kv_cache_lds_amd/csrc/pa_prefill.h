@@ -23,8 +23,9 @@ namespace pa {
 //                LDS (buffer loads with an LDS destination: lane l of an
 //                instruction fills bytes 16 l .. 16 l + 15 of one 1 KiB block,
 //                and the lane picks which 16-byte chunk of which row it
-//                fetches, so the swizzles below are free); wave w fills block
-//                w of both; keys past the visible range and pages outside the
+//                fetches, so the swizzles below are free); at D = 128 wave w
+//                fills block w of both, at D = 64 waves 0-3 the K blocks and
+//                waves 4-7 the V blocks; keys past the visible range and pages outside the
 //                pool load as zeros; page ids come through scalar loads by
 //                absolute logical index;
 //   LDS          rings of four K and four V slots (separate LDS objects), one
@@ -110,8 +111,14 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   // puts there; the lane part of every byte offset is loop-invariant.
   const CacheGeom &cg = p.geom;
   constexpr bool paged = kPaged;   // block table (else one contiguous allocation per sequence)
-  const bool loader = BPM == NW || wave < BPM;
-  const int bb = loader ? wave : 0;
+  // Every wave issues the same tile loads at the same program points: at
+  // D = 128 (eight blocks per tile) wave w fills block w of a K and of a V
+  // tile, at D = 64 (four blocks) waves 0-3 fill the K blocks and waves 4-7
+  // the V blocks.
+  constexpr bool kSplitKV = 2 * BPM == NW;
+  static_assert(BPM == NW || kSplitKV, "blocks per tile: one or two per wave");
+  const int bb = wave % BPM;
+  const bool k_wave = !kSplitKV || wave < BPM;
   const int shift = cg.page_shift;
   const uint32_t row_bytes = (uint32_t)p.hkv * D * 2;
   const uint32_t slab_bytes = paged ? row_bytes << shift : (uint32_t)cg.contig_alloc * row_bytes;
@@ -404,14 +411,16 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     const TileInfo ti_2 = tile_info(2, load_id(2));
     ti_v = tile_info(3, load_id(3));
     id_k = load_id(4);
-    if (loader) {
+    if (k_wave) {
       load_block(p.k_cache, k_slot[0], k_lane, k_blk, 0, ti_0);
-      load_block(p.v_cache, v_slot[0], v_lane, v_blk, 0, ti_0);
       load_block(p.k_cache, k_slot[1], k_lane, k_blk, 1, ti_1);
-      load_block(p.v_cache, v_slot[1], v_lane, v_blk, 1, ti_1);
       load_block(p.k_cache, k_slot[2], k_lane, k_blk, 2, ti_2);
-      load_block(p.v_cache, v_slot[2], v_lane, v_blk, 2, ti_2);
       load_block(p.k_cache, k_slot[3], k_lane, k_blk, 3, ti_v);
+    }
+    if (!kSplitKV || !k_wave) {
+      load_block(p.v_cache, v_slot[0], v_lane, v_blk, 0, ti_0);
+      load_block(p.v_cache, v_slot[1], v_lane, v_blk, 1, ti_1);
+      load_block(p.v_cache, v_slot[2], v_lane, v_blk, 2, ti_2);
     }
   }
   wait_then_barrier<0>();
@@ -433,22 +442,32 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
   // and V(t+1), read next iteration - must have landed; the newest two
   // iterations' loads stay in flight.  Full tiles: no mask.  Tail tiles: a
   // wave skips the tiles its rows cannot see.
-  constexpr int kLoadsPerIter = 2;   // vector loads of a loading wave (the page ids are scalar)
+  constexpr int kLoadsPerIter = kSplitKV ? 1 : 2;   // vector loads of a wave (page ids are scalar)
   auto iter = [&](int t, int ph, bool tail) {
-    // the tile loads: group B issues them first, group A after its MFMA
-    // phase, so that they do not delay A's matrix work.  The page id of tile
-    // t+5 is read after the MFMA phase by both groups: a scalar load still in
-    // flight would make every LDS wait of the phase a full drain (the two
-    // share a counter and scalar loads may return out of order).
+    // After its MFMA phase every wave reads the page id of tile t+5 and
+    // issues its tile loads, at one program point for both groups and every
+    // iteration.  Both placements are pinned for the compiler's waits:
+    //  - a scalar load still in flight during the MFMA phase would turn each
+    //    LDS wait of the phase into a full drain (scalar and LDS loads share a
+    //    counter, and scalar loads may return out of order);
+    //  - the waits the compiler adds for LDS-destination loads follow every
+    //    path through the loop, not just the ones a wave can take; with loads
+    //    issued at group-dependent points, or in iterations that may be
+    //    skipped, a path with fewer loads makes the explicit wait before the
+    //    barrier look too weak, and the compiler then drains every load in
+    //    flight before the reads of a slot filled three iterations earlier.
     TileInfo ti_k;
     auto issue_loads = [&]() {
       ti_k = tile_info(t + 4, id_k);
-      if (loader) {
+      if (!kSplitKV) {
         load_block(p.k_cache, k_slot[ph], k_lane, k_blk, t + 4, ti_k);
+        load_block(p.v_cache, v_slot[(ph + 3) & 3], v_lane, v_blk, t + 3, ti_v);
+      } else if (k_wave) {
+        load_block(p.k_cache, k_slot[ph], k_lane, k_blk, t + 4, ti_k);
+      } else {
         load_block(p.v_cache, v_slot[(ph + 3) & 3], v_lane, v_blk, t + 3, ti_v);
       }
     };
-    if (grp_b) issue_loads();
     const uint16_t *ks = k_slot[(ph + 1) & 3];
     const uint16_t *vs = v_slot[ph];
     const bool seen_t = !tail || t * kPTile < wave_bound;
@@ -469,8 +488,9 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     f32x16 sn;
     asm volatile("" ::"s"(id_k));   // the id read an iteration ago has landed
     mfma_phase(ks, vs, pr, sn, seen_n, seen_t, !tail);
+    __builtin_amdgcn_sched_barrier(0);
     const int id_new = load_id(t + 5);
-    if (!grp_b) issue_loads();
+    issue_loads();
     if (seen_n) {
       if (!grp_b) {
         carry = put_p(softmax(t + 1, sn, tail));
@@ -493,11 +513,13 @@ __device__ __forceinline__ void prefill_unit(const FwdParams &p, const int b, co
     iter(t + 2, 2, false);
     iter(t + 3, 3, false);
   }
+  // the masked loop runs whole groups of four (iterations past the last tile
+  // see no tile: they only load zeros and meet the barrier)
   for (; t < n_t; t += 4) {
     iter(t, 0, true);
-    if (t + 1 < n_t) iter(t + 1, 1, true);
-    if (t + 2 < n_t) iter(t + 2, 2, true);
-    if (t + 3 < n_t) iter(t + 3, 3, true);
+    iter(t + 1, 1, true);
+    iter(t + 2, 2, true);
+    iter(t + 3, 3, true);
   }
 
   if (!row_ok) return;
