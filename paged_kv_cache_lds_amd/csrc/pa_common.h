@@ -193,12 +193,15 @@ __device__ inline void find_decode_ordered(const FwdParams &p, long first, long 
   constexpr int PER = kOrderMax / NT;
   const int tid = threadIdx.x;
   int my_key[PER], my_cnt[PER];
+  SeqInfo my_si[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int s = tid + i * NT;
     int key = -1, cnt = 0;
+    my_si[i] = SeqInfo{0, 0, 0};
     if (s < p.batch) {
       const SeqInfo si = seq_info(p, s);
+      my_si[i] = si;
       const int rows = si.q_len * p.group;
       if (rows > 0 && (p.all_decode || rows <= kDecodeRows)) {
         const long tiles = decode_tiles(si.K_b);
@@ -255,6 +258,21 @@ __device__ inline void find_decode_ordered(const FwdParams &p, long first, long 
     __syncthreads();
     if (s_found[kFound * (kDecPerWg - 1)] >= 0) break;   // the last one sought is found
   }
+  // the thread that read a found sequence's metadata passes it on, sparing the
+  // workgroup a dependent reload before the unit can start
+#pragma unroll
+  for (int h = 0; h < kDecPerWg; ++h) {
+    const int sq = s_found[kFound * h];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (sq >= 0 && sq == tid + i * NT) {
+        s_found[kFound * h + 3] = my_si[i].cu_b;
+        s_found[kFound * h + 4] = my_si[i].q_len;
+        s_found[kFound * h + 5] = my_si[i].K_b;
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // Work mapping.  Units per kv head, prefill units first: a sequence whose
@@ -324,7 +342,9 @@ __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool
     u.b = s_found[slot];
     u.off = s_found[slot + 1];
     u.splits = s_found[slot + 2];
-    u.si.q_len = -1;
+    u.si.cu_b = s_found[slot + 3];
+    u.si.q_len = u.b >= 0 ? s_found[slot + 4] : -1;
+    u.si.K_b = s_found[slot + 5];
     decode = true;
     return u.b >= 0;
   }
