@@ -513,9 +513,11 @@ int32_t paged_attn_num_splits(int32_t batch, int32_t total_q, int32_t num_heads_
   // traffic and a combine.  Otherwise split each key range so the units reach
   // one per compute unit, but keep at least 8 key tiles of 32 per split (two
   // per wave) so a split's fixed cost stays amortised, and stay within the
-  // cap of 128.  A key range that allows only two such splits is not split:
-  // halving a 16-tile range saves less than the combine launch costs (batch
-  // 1-4 x context 512: one split 18.6-19.0 us, two 18.7-20.8 us).  (Measured
+  // cap of 128.  A key range that allows only two such splits is halved only
+  // while the units fill at most a quarter of the compute units (context 512:
+  // halving took batch 1 from 19.8 to 18.0 us, left batch 2 at 18.4-18.6 and
+  // took batch 4 from 19.0 to 20.8 - there the combine launch costs more than
+  // the halved range saves).  (Measured
   // over MHA decode, 32 x 128, batch 1-256 x context 512-4096: with this
   // target the chosen budget is the fastest of 1/2/4/8 or within a few
   // percent of it at every point; targeting two workgroups per compute unit
@@ -531,7 +533,8 @@ int32_t paged_attn_num_splits(int32_t batch, int32_t total_q, int32_t num_heads_
   if (units >= target) return 1;
   long s = cdiv(target, units);
   const long tiles = cdiv(max_seqlen_k, pa::kKeyTile);
-  const long cap = tiles / 8 > 2 ? tiles / 8 : 1;
+  const long cap = std::max(1L, tiles / 8);
+  if (cap == 2 && s < 4) return 1;
   s = std::min(s, cap);
   s = std::max(1L, std::min(s, (long)kMaxSplits));
   return (int32_t)s;

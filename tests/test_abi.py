@@ -137,9 +137,12 @@ def test_split_heuristic_properties():
     assert 2 <= s <= 128
     # never more splits than 8-tile chunks of the key bound, never above 128
     assert ns(1, 1, 1, 1, 128, 1, 32 * 8 * 3, 256) <= 3
-    # a range that allows only two 8-tile splits stays whole; three may split
-    assert ns(1, 1, 32, 32, 128, 1, 512, 256) == 1
-    assert ns(1, 1, 32, 32, 128, 1, 32 * 8 * 2 + 32 * 7, 256) == 1
+    # a range that allows only two 8-tile splits is halved only while the
+    # units fill at most a quarter of the compute units; three may split
+    assert ns(1, 1, 32, 32, 128, 1, 512, 256) == 2
+    assert ns(2, 2, 32, 32, 128, 1, 512, 256) == 2
+    assert ns(4, 4, 32, 32, 128, 1, 512, 256) == 1
+    assert ns(4, 4, 32, 32, 128, 1, 32 * 8 * 2 + 32 * 7, 256) == 1
     assert ns(1, 1, 32, 32, 128, 1, 32 * 8 * 3, 256) == 3
     for b in (1, 2, 4, 8, 16, 64):
         for k in (1, 100, 4096, 131072, 2**31 - 1):
