@@ -138,6 +138,44 @@ __device__ inline int seq_splits(long extra_budget, long tiles_b, long total_til
 
 __device__ inline int decode_tiles(int K_b) { return (K_b + kKeyTile - 1) / kKeyTile; }
 
+// Split budget of a batch of at most kFewSeqs sequences, one lane of wave 0
+// per sequence (dec: a decode-mode sequence, t: its key tiles).  The floors of
+// seq_splits() drop up to one unit per decode sequence; with few sequences
+// that is a large share of the budget, and the longest split, which bounds a
+// launch whose units all run at once, stays long.  The dropped units go out
+// in rounds, each to every sequence tied for the longest split (most key
+// tiles per split) that can still take one; the hand-out stops when a round
+// cannot serve its whole tie, since serving part of it would not shorten the
+// longest split.  A function of the lengths alone (not of the order of the
+// sequences), so every workgroup agrees; the total never exceeds the budget.
+constexpr int kFewSeqs = 64;
+__device__ inline void share_splits_few(int dec, int t, long n_dec, long extra,
+                                        long total_tiles, int *s_split) {
+  const int lane = threadIdx.x;
+  int s = 1, cap = 1, f = 0;
+  if (dec && extra > 0 && total_tiles > 0) {
+    f = (int)(1 + extra * t / total_tiles);
+    cap = min(max(1, t / (int)kMinSplitTiles), kMaxSplits);
+    s = min(f, cap);
+  }
+  int sum_f = f;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum_f += __shfl_xor(sum_f, o, 64);
+  long left = (extra > 0 && total_tiles > 0) ? n_dec + extra - sum_f : 0;
+  while (left > 0) {
+    const int key = (dec && s < cap) ? (t + s - 1) / s : 0;
+    int km = key;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) km = max(km, __shfl_xor(km, o, 64));
+    if (km == 0) break;
+    const long c = __popcll(__ballot(key == km));
+    if (c > left) break;
+    if (key == km) ++s;
+    left -= c;
+  }
+  if (lane < kFewSeqs) s_split[lane] = s;
+}
+
 // inclusive prefix sum over the workgroup (every thread contributes x);
 // `total` receives the workgroup sum
 template <int NW>
@@ -292,7 +330,8 @@ struct UnitInfo {
 
 template <int NT, int kDecPerWg>
 __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool &decode,
-                                   int *s_wsum, int *s_found, DecodeOrder *order) {
+                                   int *s_wsum, int *s_found, int *s_split,
+                                   DecodeOrder *order) {
   const int tid = threadIdx.x;
   const int half = kDecPerWg == 2 ? tid / (NT / 2) : 0;
   const int S = p.num_splits;
@@ -302,13 +341,20 @@ __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool
   // a mixed batch needs the key tiles only.
   long extra = 0, total_tiles = 0, n_pre = 0;
   const bool count_pre = !p.all_decode && p.unit_mode == 0;
-  if (p.unit_mode != 1 && (S > 1 || count_pre)) {
+  const bool few = S > 1 && p.unit_mode != 1 && p.batch <= kFewSeqs;
+  // a batch of at most NT sequences: pass 2 reuses what pass 1 read
+  const bool pass1 = p.unit_mode != 1 && (S > 1 || count_pre);
+  const bool reuse = pass1 && p.batch <= NT;
+  SeqInfo my_si{0, 0, 0};
+  if (pass1) {
     long n_dec = 0, tiles = 0;
+    int my_dec = 0, my_t = 0;   // this thread's sequence in the first chunk
     for (int c0 = 0; c0 < p.batch; c0 += NT) {
       const int bb = c0 + tid;
       int dec = 0, t = 0, pre = 0;
       if (bb < p.batch) {
         const SeqInfo si = seq_info(p, bb);
+        if (c0 == 0) my_si = si;
         const int rows = si.q_len * p.group;
         if (rows > 0) {
           if (is_decode(rows)) {
@@ -328,9 +374,14 @@ __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool
       n_dec += tot_d;
       tiles += tot_t;
       n_pre += tot_p;
+      if (c0 == 0) {
+        my_dec = dec;
+        my_t = t;
+      }
     }
     extra = n_dec * (S - 1);
     total_tiles = tiles;
+    if (few && tid < 64) share_splits_few(my_dec, my_t, n_dec, extra, total_tiles, s_split);
   }
   // pass 2: prefix over the units of our kind, find ours (one per half).  A
   // launch limited to one kind numbers its workgroups within that kind.
@@ -356,11 +407,11 @@ __device__ inline bool locate_unit(const FwdParams &p, int wg, UnitInfo &u, bool
     int units = 0, splits = 1;
     SeqInfo si{0, 0, 0};
     if (bb < p.batch) {
-      si = seq_info(p, bb);
+      si = reuse ? my_si : seq_info(p, bb);
       const int rows = si.q_len * p.group;
       if (rows > 0) {
         if (is_decode(rows)) {
-          splits = seq_splits(extra, decode_tiles(si.K_b), total_tiles);
+          splits = few ? s_split[bb] : seq_splits(extra, decode_tiles(si.K_b), total_tiles);
           if (!pre_wg) units = splits;
         } else if (pre_wg) {
           units = (rows + kPrefillRows - 1) / kPrefillRows;

@@ -24,6 +24,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
   __shared__ float sm_l[NW][kDecodeRows];           // of four in the unified kernel)
   __shared__ int s_wsum[NW];
   __shared__ int s_found[2 * kFound];
+  __shared__ int s_split[kFewSeqs];
 
   static_assert(NH == 1 || !kUnified, "pairs of heads only in the decode-only kernel");
   const int hgroups = p.hkv / NH;
@@ -46,15 +47,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
       have = u.b < p.batch;
     } else if (p.num_splits == 1) {
       __shared__ DecodeOrder s_order;
-      have = locate_unit<NW * 64, 1>(p, wg, u, decode, s_wsum, s_found, &s_order);
+      have = locate_unit<NW * 64, 1>(p, wg, u, decode, s_wsum, s_found, s_split, &s_order);
     } else {
-      have = locate_unit<NW * 64, 1>(p, wg, u, decode, s_wsum, s_found, nullptr);
+      have = locate_unit<NW * 64, 1>(p, wg, u, decode, s_wsum, s_found, s_split, nullptr);
     }
   } else {
     // the unified kernel keeps index order: measured, longest-first made a
     // mixed batch with 12 heads x 64 7% faster but one with 32 heads x 128 4%
     // slower (there, short units mixed with long ones keep HBM busy to the end)
-    have = locate_unit<NW * 64, 2>(p, wg, u, decode, s_wsum, s_found, nullptr);
+    have = locate_unit<NW * 64, 2>(p, wg, u, decode, s_wsum, s_found, s_split, nullptr);
   }
   // A half of the unified kernel without a decode unit still meets the one
   // workgroup barrier of the other half's decode unit.
