@@ -40,6 +40,8 @@ struct FwdParams {
   long q_stride;       // elements between consecutive tokens' q rows
   int unit_mode;       // 0: every unit; 1: prefill units only; 2: decode units only
                        // (a mixed batch split over two concurrent launches)
+  int uniform_q_tiles; // > 0: every sequence has the same query length, of this many
+                       // prefill units (query tiles); units map by block index
 };
 
 struct AppendParams {

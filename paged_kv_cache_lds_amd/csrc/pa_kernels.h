@@ -51,6 +51,21 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     } else {
       have = locate_unit<NW * 64, 1>(p, wg, u, decode, s_wsum, s_found, s_split, nullptr);
     }
+  } else if (p.uniform_q_tiles > 0) {
+    // Every sequence has the same query length (more rows than a decode
+    // unit): the units follow from the block index in the order the search
+    // below would give them (sequence by sequence, a sequence's last and
+    // heaviest query tile first), without its passes over the metadata.
+    // Measured, attention only: causal prefill 4x2048 197 -> 187 us, 4x8192
+    // 2181 -> 2079 us.  The heaviest tiles of every sequence first instead
+    // ran 1-5% slower than this order, under which the query tiles of one
+    // sequence run at the same time and can share its K/V in L2.
+    have = wg < p.batch * p.uniform_q_tiles;
+    u.b = wg / p.uniform_q_tiles;
+    u.off = wg % p.uniform_q_tiles;
+    u.splits = 1;
+    u.si.q_len = -1;
+    decode = false;
   } else {
     // the unified kernel keeps index order: measured, longest-first made a
     // mixed batch with 12 heads x 64 7% faster but one with 32 heads x 128 4%
@@ -139,6 +154,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
                                    sm_m + kWaves, sm_l + kWaves);
     } else {
       const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
+      if (u.off >= n_qt) return;   // only with a query longer than max_seqlen_q promised
       if (p.geom.table != nullptr)
         prefill_unit<DT, D, true>(p, u.b, g, n_qt - 1 - u.off, si, pool);
       else

@@ -43,12 +43,20 @@ struct Plan {
   size_t ws_bytes = 0;
   size_t o_part_off = 0, lse_part_off = 0, rsplit_off = 0;
   int max_seqlen_k = 0;
+  int uniform_q_tiles = 0;   // > 0: equal query lengths, prefill units by block index
 };
 
 inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 inline int ilog2(int x) { int s = 0; while ((1 << s) < x) ++s; return s; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+// PAGED_ATTN_PREFILL_SEARCH=1: prefill units found by the device search even
+// when every sequence has the same query length
+bool prefill_search_forced() {
+  const char *e = std::getenv("PAGED_ATTN_PREFILL_SEARCH");
+  return e != nullptr && std::strcmp(e, "1") == 0;
+}
 
 // PAGED_ATTN_HEAD_PAIRS=0: decode units over one kv head only
 bool pair_units_disabled() {
@@ -208,6 +216,14 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
   const long pre_per_head = cdiv(total_rows, pa::kPrefillRows) + n_p - 1;
   if (!pl.all_decode) units_per_head = cdiv(units_per_head, 2) + pre_per_head;
   pl.grid = units_per_head * (a->num_heads_kv / pl.pair);
+  // Every sequence holds max_seqlen_q new tokens (their sum is total_q and
+  // none exceeds max_seqlen_q) and more rows than a decode unit: the unified
+  // kernel's prefill units follow from the block index, one per query tile.
+  if (!pl.all_decode && (long)a->total_q == (long)a->batch * a->max_seqlen_q &&
+      (long)a->max_seqlen_q * group > pa::kDecodeRows && !prefill_search_forced()) {
+    pl.uniform_q_tiles = (int)cdiv((long)a->max_seqlen_q * group, pa::kPrefillRows);
+    pl.grid = (long)a->batch * pl.uniform_q_tiles * a->num_heads_kv;
+  }
   // A decode-mode sequence has 1 .. kDecodeRows / group new tokens.  The
   // shortest sequence has at least total_q - (batch - 1) * max_seqlen_q; if
   // that already exceeds a decode unit, every sequence is prefill-mode.
@@ -404,6 +420,7 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   p.all_decode = pl.all_decode;
   p.rot = rotary_of(a);
   p.unit_mode = 0;
+  p.uniform_q_tiles = 0;
   if (pl.grid > 0x7fffffffL || pl.grid_dec > 0x7fffffffL || pl.grid_pre > 0x7fffffffL)
     return PA_ERR_SHAPE;
   // every row is appended before any attention launch, on either stream,
@@ -447,6 +464,7 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
     const bool launched = hipGetLastError() == hipSuccess;
     if (hipStreamWaitEvent(stream, f.join, 0) != hipSuccess || !launched) return PA_ERR_HIP;
   } else {
+    p.uniform_q_tiles = pl.uniform_q_tiles;
     hipLaunchKernelGGL((pa::attn_fwd_kernel<DT, D>), dim3((unsigned)pl.grid), dim3(pa::kUThreads), 0,
                        stream, p);
   }

@@ -442,6 +442,27 @@ def test_decode_varlen_unit_order(batch, monkeypatch):
         assert torch.equal(o1, full_out[s_:e_]) and torch.equal(l1, full_lse[s_:e_]), f"sequence {b}"
 
 
+@pytest.mark.parametrize("nq,hq,hkv,hd,dtype,P", [
+    (300, 48, 16, 64, "bf16", 32),     # group 3: a token's rows straddle query tiles
+    (1000, 32, 32, 128, "f16", None),  # contiguous cache
+    (5, 64, 8, 128, "bf16", 16),       # 40 rows: one query tile per sequence
+])
+def test_equal_query_lengths_map_like_the_search(nq, hq, hkv, hd, dtype, P, monkeypatch):
+    # with every sequence at max_seqlen_q new tokens the unified kernel maps
+    # its prefill units by block index instead of searching the metadata: the
+    # bits must be those of the searched mapping (and the oracle's to the bar)
+    rng = np.random.default_rng(5400 + nq)
+    lens = [nq + int(x) for x in rng.integers(0, 600, 5)]   # every query row sees keys
+    c = Case(name=f"equal_q_{nq}_{hq}x{hkv}x{hd}", q_lens=[nq] * 5, cache_seqlens=lens,
+             num_heads_q=hq, num_heads_kv=hkv, head_dim=hd, dtype=dtype, page_size=P,
+             contig_alloc=0 if P else 2048, append=False, causal=True, seed=5400 + nq)
+    inp, _ = run_parity(c)
+    direct = gpu_call(inp)
+    monkeypatch.setenv("PAGED_ATTN_PREFILL_SEARCH", "1")
+    searched = gpu_call(inp)
+    assert torch.equal(direct[0], searched[0]) and torch.equal(direct[1], searched[1])
+
+
 def test_zero_length_padding_slots():
     c = wl.unified_varlen(50, heads=12, head_dim=64)
     c.q_lens = c.q_lens[:5]
