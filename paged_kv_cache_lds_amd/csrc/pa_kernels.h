@@ -45,6 +45,17 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
       u.splits = 1;
       u.si.q_len = -1;
       have = u.b < p.batch;
+    } else if (p.batch == 1 && p.all_decode) {
+      // one sequence: the whole split budget is its own, so its split count
+      // follows from its length alone (what the search below would find) and
+      // workgroup wg takes split wg
+      const SeqInfo si = seq_info(p, 0);
+      const int t = decode_tiles(si.K_b);
+      u.b = 0;
+      u.off = wg;
+      u.splits = si.q_len > 0 ? seq_splits(p.num_splits - 1, t, t) : 0;
+      u.si = si;
+      have = wg < u.splits;
     } else if (p.num_splits == 1) {
       __shared__ DecodeOrder s_order;
       have = locate_unit<NW * 64, 1>(p, wg, u, decode, s_wsum, s_found, s_split, &s_order);

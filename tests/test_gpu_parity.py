@@ -463,6 +463,32 @@ def test_equal_query_lengths_map_like_the_search(nq, hq, hkv, hd, dtype, P, monk
     assert torch.equal(direct[0], searched[0]) and torch.equal(direct[1], searched[1])
 
 
+def test_single_sequence_decode_matches_a_padded_batch():
+    # a one-sequence decode batch maps its splits by block index (no unit
+    # search); the same sequence beside a (0, 0) padding slot goes through the
+    # search with the same budget per decode sequence: the same bits
+    rng = np.random.default_rng(5500)
+    for ctx in (1, 300, 513, 4097):
+        c = Case(name=f"single_seq_{ctx}", q_lens=[1, 0], cache_seqlens=[ctx, 0], num_heads_q=32,
+                 num_heads_kv=8, head_dim=128, dtype="bf16", page_size=16, append=True,
+                 causal=True, seed=int(rng.integers(1 << 30)))
+        inp = make_inputs(c, "cuda")
+        kc0, vc0 = inp.k_cache.clone(), inp.v_cache.clone()
+        for s in (1, 2, 3, 8, 64):
+            say(f"  ctx {ctx} num_splits {s}")
+            inp.k_cache.copy_(kc0); inp.v_cache.copy_(vc0)
+            two = gpu_call(inp, num_splits=s)
+            inp.k_cache.copy_(kc0); inp.v_cache.copy_(vc0)
+            one = pa.paged_attn_fwd(inp.q, inp.k_cache, inp.v_cache, inp.block_table[:1].contiguous(),
+                                    inp.cache_seqlens[:1].contiguous(), inp.cu_seqlens_q[:2].contiguous(),
+                                    max_seqlen_q=1, k_new=inp.k_new, v_new=inp.v_new, causal=True,
+                                    num_splits=s)
+            torch.cuda.synchronize()
+            assert torch.equal(one[0], two[0]) and torch.equal(one[1], two[1]), f"ctx {ctx} S {s}"
+        ref_out, ref_lse, _, _ = oracle_call(inp, host(kc0), host(vc0))
+        check_against_oracle(one[0], one[1], ref_out, ref_lse, f"single sequence ctx {ctx}")
+
+
 def test_zero_length_padding_slots():
     c = wl.unified_varlen(50, heads=12, head_dim=64)
     c.q_lens = c.q_lens[:5]
