@@ -42,6 +42,8 @@ struct FwdParams {
                        // (a mixed batch split over two concurrent launches)
   int uniform_q_tiles; // > 0: every sequence has the same query length, of this many
                        // prefill units (query tiles); units map by block index
+  int full_search;     // 1: units always from the workgroup-wide search (no shortcut
+                       // for one sequence or for a few)
 };
 
 struct AppendParams {
@@ -151,9 +153,7 @@ __device__ inline int decode_tiles(int K_b) { return (K_b + kKeyTile - 1) / kKey
 // longest split.  A function of the lengths alone (not of the order of the
 // sequences), so every workgroup agrees; the total never exceeds the budget.
 constexpr int kFewSeqs = 64;
-__device__ inline void share_splits_few(int dec, int t, long n_dec, long extra,
-                                        long total_tiles, int *s_split) {
-  const int lane = threadIdx.x;
+__device__ inline int few_splits(int dec, int t, long n_dec, long extra, long total_tiles) {
   int s = 1, cap = 1, f = 0;
   if (dec && extra > 0 && total_tiles > 0) {
     f = (int)(1 + extra * t / total_tiles);
@@ -175,7 +175,12 @@ __device__ inline void share_splits_few(int dec, int t, long n_dec, long extra,
     if (key == km) ++s;
     left -= c;
   }
-  if (lane < kFewSeqs) s_split[lane] = s;
+  return s;
+}
+__device__ inline void share_splits_few(int dec, int t, long n_dec, long extra,
+                                        long total_tiles, int *s_split) {
+  const int s = few_splits(dec, t, n_dec, extra, total_tiles);
+  if (threadIdx.x < kFewSeqs) s_split[threadIdx.x] = s;
 }
 
 // inclusive prefix sum over the workgroup (every thread contributes x);
@@ -313,6 +318,79 @@ __device__ inline void find_decode_ordered(const FwdParams &p, long first, long 
     }
   }
   __syncthreads();
+}
+
+// Decode unit `first` of a decode-only launch over at most kFewSeqs
+// sequences, found by wave 0 alone: one lane per sequence, wave shuffles in
+// place of the workgroup scans and barriers of locate_unit and
+// find_decode_ordered, with the same units in the same order (longest first
+// with one unit per sequence, index order with a split budget) and the same
+// split counts.  The result goes to s_found (kFound ints; sequence -1: no
+// unit) for the caller to publish with one barrier.
+__device__ inline int wave_excl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  return incl - x;
+}
+__device__ inline int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ inline void find_decode_few(const FwdParams &p, long first, bool longest_first,
+                                       int *s_found) {
+  const int lane = threadIdx.x;   // wave 0
+  const int S = p.num_splits;
+  SeqInfo si{0, 0, 0};
+  int dec = 0, t = 0;
+  if (lane < p.batch) {
+    si = seq_info(p, lane);
+    const int rows = si.q_len * p.group;
+    if (rows > 0 && (p.all_decode || rows <= kDecodeRows)) {
+      dec = 1;
+      t = decode_tiles(si.K_b);
+    }
+  }
+  int cnt = dec;
+  if (S > 1) {
+    const long n_dec = wave_sum(dec);
+    const long tiles = wave_sum(t);
+    const int s = few_splits(dec, t, n_dec, n_dec * (S - 1), tiles);
+    cnt = dec ? s : 0;
+  }
+  int excl;   // units before this sequence's first
+  if (S == 1 && longest_first) {
+    // one unit per decode sequence, by rank: most key tiles first, ties by
+    // index (every decode sequence ranks before every other one)
+    const int key = dec ? t : -1;
+    const int next = __shfl_down(key, 1, 64);
+    if (!__any(lane + 1 < p.batch && key < next)) {
+      excl = lane;
+    } else {
+      excl = 0;
+      for (int s2 = 0; s2 < p.batch; ++s2) {
+        const int k2 = __shfl(key, s2, 64);
+        excl += (k2 > key) | ((k2 == key) & (s2 < lane));
+      }
+    }
+  } else {
+    excl = wave_excl_scan(cnt);
+  }
+  const bool found = cnt > 0 && first >= excl && first < excl + cnt;
+  if (found) {
+    s_found[0] = lane;
+    s_found[1] = (int)(first - excl);
+    s_found[2] = cnt;
+    s_found[3] = si.cu_b;
+    s_found[4] = si.q_len;
+    s_found[5] = si.K_b;
+  }
+  if (__ballot(found) == 0 && lane == 0) s_found[0] = -1;
 }
 
 // Work mapping.  Units per kv head, prefill units first: a sequence whose

@@ -45,7 +45,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
       u.splits = 1;
       u.si.q_len = -1;
       have = u.b < p.batch;
-    } else if (p.batch == 1 && p.all_decode) {
+    } else if (p.batch == 1 && p.all_decode && !p.full_search) {
       // one sequence: the whole split budget is its own, so its split count
       // follows from its length alone (what the search below would find) and
       // workgroup wg takes split wg
@@ -56,6 +56,17 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
       u.splits = si.q_len > 0 ? seq_splits(p.num_splits - 1, t, t) : 0;
       u.si = si;
       have = wg < u.splits;
+    } else if (p.batch <= kFewSeqs && (p.all_decode || p.unit_mode == 2) && !p.full_search) {
+      // a few sequences: the search in one wave, published with one barrier
+      if (threadIdx.x < 64) find_decode_few(p, wg, p.num_splits == 1, s_found);
+      __syncthreads();
+      u.b = s_found[0];
+      u.off = s_found[1];
+      u.splits = s_found[2];
+      u.si.cu_b = s_found[3];
+      u.si.q_len = u.b >= 0 ? s_found[4] : -1;
+      u.si.K_b = s_found[5];
+      have = u.b >= 0;
     } else if (p.num_splits == 1) {
       __shared__ DecodeOrder s_order;
       have = locate_unit<NW * 64, 1>(p, wg, u, decode, s_wsum, s_found, s_split, &s_order);

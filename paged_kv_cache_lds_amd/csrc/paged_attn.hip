@@ -51,10 +51,11 @@ inline int ilog2(int x) { int s = 0; while ((1 << s) < x) ++s; return s; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline long cdiv(long a, long b) { return (a + b - 1) / b; }
 
-// PAGED_ATTN_PREFILL_SEARCH=1: prefill units found by the device search even
-// when every sequence has the same query length
-bool prefill_search_forced() {
-  const char *e = std::getenv("PAGED_ATTN_PREFILL_SEARCH");
+// PAGED_ATTN_FULL_SEARCH=1: every unit found by the workgroup-wide search of
+// the metadata (no block-index mapping for equal query lengths or a single
+// sequence, no one-wave search for a few sequences); the same results
+bool full_search_forced() {
+  const char *e = std::getenv("PAGED_ATTN_FULL_SEARCH");
   return e != nullptr && std::strcmp(e, "1") == 0;
 }
 
@@ -220,7 +221,7 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
   // none exceeds max_seqlen_q) and more rows than a decode unit: the unified
   // kernel's prefill units follow from the block index, one per query tile.
   if (!pl.all_decode && (long)a->total_q == (long)a->batch * a->max_seqlen_q &&
-      (long)a->max_seqlen_q * group > pa::kDecodeRows && !prefill_search_forced()) {
+      (long)a->max_seqlen_q * group > pa::kDecodeRows && !full_search_forced()) {
     pl.uniform_q_tiles = (int)cdiv((long)a->max_seqlen_q * group, pa::kPrefillRows);
     pl.grid = (long)a->batch * pl.uniform_q_tiles * a->num_heads_kv;
   }
@@ -421,6 +422,7 @@ pa_status launch_attention(const pa_fwd_args *a, const Plan &pl, hipStream_t str
   p.rot = rotary_of(a);
   p.unit_mode = 0;
   p.uniform_q_tiles = 0;
+  p.full_search = full_search_forced() ? 1 : 0;
   if (pl.grid > 0x7fffffffL || pl.grid_dec > 0x7fffffffL || pl.grid_pre > 0x7fffffffL)
     return PA_ERR_SHAPE;
   // every row is appended before any attention launch, on either stream,

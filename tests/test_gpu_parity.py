@@ -458,7 +458,7 @@ def test_equal_query_lengths_map_like_the_search(nq, hq, hkv, hd, dtype, P, monk
              contig_alloc=0 if P else 2048, append=False, causal=True, seed=5400 + nq)
     inp, _ = run_parity(c)
     direct = gpu_call(inp)
-    monkeypatch.setenv("PAGED_ATTN_PREFILL_SEARCH", "1")
+    monkeypatch.setenv("PAGED_ATTN_FULL_SEARCH", "1")
     searched = gpu_call(inp)
     assert torch.equal(direct[0], searched[0]) and torch.equal(direct[1], searched[1])
 
@@ -487,6 +487,27 @@ def test_single_sequence_decode_matches_a_padded_batch():
             assert torch.equal(one[0], two[0]) and torch.equal(one[1], two[1]), f"ctx {ctx} S {s}"
         ref_out, ref_lse, _, _ = oracle_call(inp, host(kc0), host(vc0))
         check_against_oracle(one[0], one[1], ref_out, ref_lse, f"single sequence ctx {ctx}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4, 16])
+def test_few_sequence_search_matches_the_block_search(splits, monkeypatch):
+    # up to 64 sequences, the decode kernel finds its units in one wave; with
+    # PAGED_ATTN_FULL_SEARCH=1 the workgroup-wide search runs instead: the
+    # same units and split counts, so the same bits (unsorted lengths with
+    # ties, a q_len-0 slot inside)
+    rng = np.random.default_rng(5600 + splits)
+    lens = [int(x) for x in rng.integers(0, 3000, 40)]
+    lens[5] = lens[9] = lens[30] = 1500                     # ties
+    q_lens = [1] * 40
+    q_lens[12], lens[12] = 0, 0                               # a padding slot inside
+    c = Case(name=f"few_seq_search_S{splits}", q_lens=q_lens, cache_seqlens=lens, num_heads_q=32,
+             num_heads_kv=8, head_dim=128, dtype="f16", page_size=16, append=False, causal=True,
+             num_splits=splits, seed=5600 + splits)
+    inp, _ = run_parity(c, splits=(splits,))
+    wave = gpu_call(inp, num_splits=splits)
+    monkeypatch.setenv("PAGED_ATTN_FULL_SEARCH", "1")
+    block = gpu_call(inp, num_splits=splits)
+    assert torch.equal(wave[0], block[0]) and torch.equal(wave[1], block[1])
 
 
 def test_zero_length_padding_slots():
