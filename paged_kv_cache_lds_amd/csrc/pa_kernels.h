@@ -176,7 +176,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
                                    sm_m + kWaves, sm_l + kWaves);
     } else {
       const int n_qt = (rows_b + kPrefillRows - 1) / kPrefillRows;
-      if (u.off >= n_qt) return;   // only with a query longer than max_seqlen_q promised
+      // a query tile past the sequence's rows: only when some sequence broke
+      // the q_len <= max_seqlen_q bound, so that this one is shorter than the
+      // equal-length mapping assumed
+      if (u.off >= n_qt) return;
       if (p.geom.table != nullptr)
         prefill_unit<DT, D, true>(p, u.b, g, n_qt - 1 - u.off, si, pool);
       else
