@@ -538,10 +538,23 @@ def main():
                               v_new=pin.v_new, causal=True, out=pout, softmax_lse=plse)
 
         pms = time_calls(pstep, max(3, args.steps // 2), 2, torch)
+        # the attention alone over the same keys (the appended rows are in the
+        # pages by now): the prefill kernel without the append's copy
+        seq_after = (pin.cache_seqlens + pc.q_lens[0]).contiguous()
+
+        def pattn():
+            pa.paged_attn_fwd(pin.q, pin.k_cache, pin.v_cache, pin.block_table, seq_after,
+                              pin.cu_seqlens_q, max_seqlen_q=pin.max_seqlen_q, causal=True,
+                              out=pout, softmax_lse=plse)
+
+        ams = time_calls(pattn, max(3, args.steps // 2), 2, torch)
         fl = causal_flops(pc)
         tfs = fl / (pms * 1e-3) / 1e12
+        atfs = fl / (ams * 1e-3) / 1e12
         prefill = {"workload": pc.name, "ms": round(pms, 4), "tflops": round(tfs, 2),
                    "peak": MFMA_F16_PEAK_TFS, "frac": round(tfs / MFMA_F16_PEAK_TFS, 4),
+                   "attention_only_ms": round(ams, 4),
+                   "attention_only_frac": round(atfs / MFMA_F16_PEAK_TFS, 4),
                    "flops_per_call": fl}
 
     # ---- measured references on this GPU: a large fp16 GEMM through the
