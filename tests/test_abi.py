@@ -132,9 +132,16 @@ def test_split_heuristic_properties():
     ns = pa.paged_attn_num_splits
     # the machine is already full -> no split
     assert ns(256, 256, 32, 32, 128, 1, 4096, 256) == 1
-    # long-context GQA decode with few sequences -> splits
+    # long-context GQA decode with few sequences -> splits, up to two units
+    # per compute unit while every split keeps >= 64 key tiles
     s = ns(8, 8, 64, 8, 128, 1, 131072, 256)
     assert 2 <= s <= 128
+    assert s == 8
+    assert ns(16, 16, 64, 8, 128, 1, 12288, 256) == 4
+    assert ns(16, 16, 64, 8, 128, 1, 2048, 256) == 2        # 64-tile splits: one unit per CU
+    assert ns(32, 32, 64, 8, 128, 1, 8192, 256) == 1        # the CUs are already full
+    # MHA keeps one unit per compute unit
+    assert ns(4, 4, 32, 32, 128, 1, 8192, 256) == 2
     # never more splits than 8-tile chunks of the key bound, never above 128
     assert ns(1, 1, 1, 1, 128, 1, 32 * 8 * 3, 256) <= 3
     # a range that allows only two 8-tile splits is halved only while the
