@@ -155,22 +155,26 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
   const int row_lim =
       row_ok ? min(row_key_bound(lr, group, si.q_len, si.K_b, p.causal), key_end_w) : 0;
 
+  // The query rows (and the fused rotary embedding's operands, at the
+  // token's position K_b - q_len + tok) are fetched after the first page ids
+  // (below): loads retire in order, so the first tile's loads then wait for
+  // the page ids only; the rows are needed only once that tile has landed.
   u32x4 qf[DS];
-  {
-    const uint16_t *qrow = p.q + (long)(si.cu_b + tok) * p.q_stride + (long)h * D;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-      qf[ds] = row_ok ? load16(qrow + (ds * 4 + lg) * 8) : u32x4{0u, 0u, 0u, 0u};
-  }
-  // fused rotary embedding of the query row, at the token's position
-  // K_b - q_len + tok: its operands are fetched with the row, and applied once
-  // the first tile's loads are out (see below)
   const bool rot_q = p.rot.cos != nullptr;
   const int rot_pos = row_ok ? si.K_b - si.q_len + tok : -1;
   RotFetch<DS> rotf;
-  if (rot_q)
-    rot_fetch(p.rot, p.q + (long)(si.cu_b + tok) * p.q_stride + (long)h * D, lg * 8, 32, rot_pos,
-              rotf);
+  auto fetch_q = [&]() {
+    // a lane without a row reads the unit's first row (token 0 of the
+    // sequence, head g * group: always there) and drops it, so that no load
+    // sits behind a branch and the first tile waits for the page ids only
+    const uint16_t *qrow = p.q + (long)(si.cu_b + tok) * p.q_stride + (long)h * D;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const u32x4 v = load16(qrow + (ds * 4 + lg) * 8);
+      qf[ds] = row_ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (rot_q) rot_fetch(p.rot, qrow, lg * 8, 32, rot_pos, rotf);
+  };
 
   const CacheGeom &cg = p.geom;
   const bool paged = cg.table != nullptr;
@@ -338,6 +342,7 @@ __device__ __forceinline__ void decode_unit(const FwdParams &p, const int b, con
     u32x4 ka[NLD], va_[NLD], kb_[NLD], vb_[NLD];
     int ids_a = load_ids(w_begin);
     int ids_b = load_ids(w_begin + 1);
+    fetch_q();
     issue(w_begin, ka, va_, ids_a);
     if (rot_q) rot_apply<DT>(p.rot, lg * 8, 32, rot_pos, qf, rotf);
     ids_a = load_ids(w_begin + 2);
