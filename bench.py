@@ -403,8 +403,8 @@ def main():
         sweep(args.sweep, args.reps, args.sweep_out)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence / kv head / key range, see the design notes).",
+        print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (across GPUs the "
+              "path would shard by sequence, kv head or key range, with no collective on it).",
               file=sys.stderr)
         sys.exit(2)
 

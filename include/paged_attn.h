@@ -52,7 +52,7 @@ typedef enum pa_status {
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
   PA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
   PA_ERR_DTYPE = 3,       /* dtype is not PA_F16 / PA_BF16 */
-  PA_ERR_UNSUPPORTED = 4, /* head_dim or page size this build does not serve, or one
+  PA_ERR_UNSUPPORTED = 4, /* head_dim or page size the library does not serve, or one
                              page (contiguous mode: one sequence's allocation) spans
                              2 GiB or more */
   PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than paged_attn_workspace_size */
