@@ -396,7 +396,7 @@ def main():
     ap.add_argument("--sweep", choices=["copy", "decode", "gqa", "prefill", "unified", "graph", "rotary",
                                         "multitoken"],
                     help="run a measurement sweep instead of the headline line")
-    ap.add_argument("--sweep-out", default="gpurun_out/sweep.jsonl")
+    ap.add_argument("--sweep-out", default="sweep.jsonl")
     ap.add_argument("--reps", type=int, default=10)
     args = ap.parse_args()
     if args.sweep:
