@@ -82,6 +82,41 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
   const int vec_per_row = p.hkv * p.head_dim / 8;   // 16-byte vectors per token row
   const int L = p.cache_seqlens[b];
   const int work = ntok * vec_per_row * 2;
+  if (p.rot.cos == nullptr) {
+    // Plain copy: a thread first loads all its vectors of a batch (their
+    // sources do not depend on the pages), then finds each target and stores
+    // - loads and stores to possibly aliasing buffers would otherwise
+    // alternate, one load in flight per thread.
+    constexpr int kPer = 4;
+    for (int base = 0; base < work; base += kPer * kThreads) {
+      u32x4 buf[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int idx = base + j * kThreads + threadIdx.x;
+        if (idx < work) {
+          const int which = idx / (ntok * vec_per_row);
+          const int rem = idx - which * ntok * vec_per_row;
+          const int t = rem / vec_per_row;
+          const int v = rem - t * vec_per_row;
+          const long src = (long)(cu_b + tok0 + t) * (which ? p.vn_stride : p.kn_stride) + v * 8;
+          buf[j] = load16((which ? p.v_new : p.k_new) + src);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int idx = base + j * kThreads + threadIdx.x;
+        if (idx < work) {
+          const int which = idx / (ntok * vec_per_row);
+          const int rem = idx - which * ntok * vec_per_row;
+          const int t = rem / vec_per_row;
+          const int v = rem - t * vec_per_row;
+          const long prow = physical_row(p.geom, b, L + tok0 + t);
+          if (prow >= 0) store16((which ? p.v_cache : p.k_cache) + (prow * vec_per_row + v) * 8, buf[j]);
+        }
+      }
+    }
+    return;
+  }
   for (int idx = threadIdx.x; idx < work; idx += kThreads) {
     const int which = idx / (ntok * vec_per_row);     // 0: K, 1: V
     const int rem = idx - which * ntok * vec_per_row;
