@@ -189,15 +189,24 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
   const int group = a->num_heads_q / a->num_heads_kv;
   pl.max_seqlen_k = key_bound(a);
   pl.all_decode = (long)a->max_seqlen_q * group <= pa::kDecodeRows;
-  // Decode units over pairs of adjacent kv heads read 512-byte row slices
-  // (head_dim 128) instead of 256: when every sequence's rows fit twice into
-  // a unit, the kv heads pair up, and the batch still gives every compute
-  // unit at least two pair units (measured on MHA decode: +3% at 256 x 4096,
-  // +1.5% at 64 x 2048, 3% on a 64-sequence varlen batch; 6-7% slower at
-  // 512 units and below, where halving the units costs parallelism).
+  // Decode units over pairs of adjacent kv heads read row slices twice as
+  // wide (512 bytes at head_dim 128, 256 at 64): when every sequence's rows
+  // fit twice into a unit, the kv heads pair up, provided that the batch
+  // still gives every compute unit at least two pair units and that the pair
+  // units leave no partial round of workgroups the one-head units would not.
+  // A CU holds two decode workgroups, so units run in rounds of 2 x CUs, and
+  // a pair unit takes two one-head units' time: pairs pay only where
+  // 2 * rounds(pairs) <= rounds(one-head units).  Measured (one-head -> pair
+  // units): +2 to +5% at head_dim 128 and +9 to +13% at 64 where both fill
+  // whole rounds (e.g. 256 x 4096 MHA, 64 x 2048 with 32 heads of 64), but
+  // 5-18% slower at 128 where pairs end on a part-filled round (48, 100 and
+  // 40 sequences x 32 heads; 160 x 8 kv heads) and 7-23% slower at 64 (96,
+  // 128 and 200 sequences x 12 heads).
+  const long units1 = (long)a->batch * a->num_heads_kv;
+  const long per_round = 2L * num_cus;
   pl.pair = pl.all_decode && a->num_heads_kv % 2 == 0 &&
-                    2L * a->max_seqlen_q * group <= pa::kDecodeRows &&
-                    (long)a->batch * a->num_heads_kv >= 4L * num_cus && !pair_units_disabled()
+                    2L * a->max_seqlen_q * group <= pa::kDecodeRows && units1 >= 4L * num_cus &&
+                    2 * cdiv(units1 / 2, per_round) <= cdiv(units1, per_round) && !pair_units_disabled()
                 ? 2
                 : 1;
   pl.splits = a->num_splits > 0
