@@ -155,12 +155,25 @@ def test_split_heuristic_properties():
         for k in (1, 100, 4096, 131072, 2**31 - 1):
             v = ns(b, b, 8, 1, 128, 1, k, 256)
             assert 1 <= v <= 128
-    # more work units never ask for more splits
+    # below one unit per compute unit, more work units never ask for more
+    # splits; from one unit per compute unit on, at most two
     prev = 129
-    for b in range(1, 600, 7):
+    for b in range(1, 8):
         v = ns(b, b, 32, 32, 128, 1, 65536, 256)
         assert v <= prev
         prev = v
+    for b in range(8, 600, 7):
+        assert ns(b, b, 32, 32, 128, 1, 65536, 256) in (1, 2)
+    # one to four units per compute unit that leave some compute units a unit
+    # more than others (1.5 or 2.5 per CU) split in two; whole units per CU,
+    # short key ranges and four or more units per CU stay whole
+    assert ns(12, 12, 32, 32, 128, 1, 4096, 256) == 2       # 384 units
+    assert ns(20, 20, 32, 32, 128, 1, 8192, 256) == 2       # 640 units
+    assert ns(48, 48, 64, 8, 128, 1, 8192, 256) == 2        # 384 units, grouped heads
+    for b in (8, 16, 24, 40, 48, 80):
+        assert ns(b, b, 32, 32, 128, 1, 4096, 256) == 1
+    assert ns(12, 12, 32, 32, 128, 1, 1024, 256) == 1       # 32-tile splits would not fit
+    assert ns(36, 36, 32, 32, 128, 1, 4096, 256) == 1       # 1152 units: 4.5 per CU
     # depends only on its arguments (pure, host-known sizes)
     assert ns(8, 8, 64, 8, 128, 1, 131072, 256) == ns(8, 8, 64, 8, 128, 1, 131072, 256)
     # degenerate inputs
