@@ -205,8 +205,10 @@ pa_status paged_attn_fwd(const pa_fwd_args *args, void *stream);
  * that forbid allocation.  Same arguments, kernels and results (bit for bit)
  * as paged_attn_fwd, except that args->workspace / workspace_bytes and
  * args->aux_stream are ignored: the split-KV scratch is a static device array
- * of the library (64 MiB = 67108864 bytes), one per device, held from the library's load on the device until the process ends,
- * and a mixed batch always runs as one launch on `stream`.  The call makes no
+ * of the library (64 MiB = 67108864 bytes), one per device, held from the
+ * library's load on the device until the process ends, and a mixed batch
+ * never forks onto a second stream: all of its launches (by default the
+ * prefill units, then the decode units) run on `stream`.  The call makes no
  * allocation of any kind (it creates no events either) and never
  * synchronises; PAGED_ATTN_DEBUG is not honoured here.  A call whose plan
  * needs more scratch than the array holds returns PA_ERR_SCRATCH before any

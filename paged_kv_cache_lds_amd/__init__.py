@@ -372,8 +372,9 @@ def paged_attn_fwd_noalloc(q, k_cache, v_cache, block_table, cache_seqlens, cu_s
     """The allocation-free entry point: as paged_attn_fwd, with the caller's
     ``out`` / ``softmax_lse`` (required) and the library's static split-KV
     scratch in place of a workspace; neither the binding nor the library
-    allocates anything, and a mixed batch runs as one launch.  Calls that
-    overlap on one GPU share the scratch and must be serialised."""
+    allocates anything, and every launch of a mixed batch runs on ``stream``
+    (none is forked onto a second stream).  Calls that overlap on one GPU
+    share the scratch and must be serialised."""
     if out is None or softmax_lse is None:
         raise ValueError("paged_attn_fwd_noalloc writes into the caller's out and softmax_lse")
     args = make_args(q, k_cache, v_cache, block_table, cache_seqlens, cu_seqlens_q,
