@@ -133,6 +133,16 @@ def test_mha_decode_batch_sweep_corner(P):
     run_fullsize(c, {3: [0], 200: [0]}, causal=False)
 
 
+@pytest.mark.parametrize("batch", [12, 20])
+def test_mha_decode_uneven_units_split_in_two(batch):
+    # 384 and 640 one-head units (1.5 and 2.5 per compute unit of an MI355X):
+    # the heuristic gives every key range two splits; the bench step's shape
+    # otherwise (one appended token, 4096 cached)
+    assert pa.paged_attn_num_splits(batch, batch, 32, 32, 128, 1, 4097, 256) == 2
+    c = wl.mha_decode(batch, 4096, append=True)
+    run_fullsize(c, {0: [0], batch // 2: [0], batch - 1: [0]}, causal=False)
+
+
 @pytest.mark.parametrize("paged", [True, False])
 def test_gqa_long_split_allocation_bound(paged):
     # batch 8, 64/8 heads, lengths in [2048, 32768] inside a 131072-token
