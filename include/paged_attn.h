@@ -248,8 +248,9 @@ size_t paged_attn_workspace_size(const pa_fwd_args *args);
 
 /*
  * paged_attn_splits_for - the split-KV count paged_attn_fwd will use for these
- * arguments (the forced value, or the heuristic on this device), or -1 for
- * invalid sizes.  Reads sizes and flags only, like paged_attn_workspace_size;
+ * arguments (the forced value; else 1 when the plan runs decode units over
+ * pairs of kv heads, and paged_attn_num_splits on this device otherwise), or
+ * -1 for invalid sizes.  Reads sizes and flags only, like paged_attn_workspace_size;
  * host only apart from one cached device-attribute query.
  */
 int32_t paged_attn_splits_for(const pa_fwd_args *args);

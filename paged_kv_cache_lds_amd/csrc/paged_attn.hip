@@ -194,8 +194,8 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
   // fit twice into a unit, the kv heads pair up, provided that the batch
   // still gives every compute unit at least two pair units and that the pair
   // units leave no partial round of workgroups the one-head units would not.
-  // A CU holds two decode workgroups, so units run in rounds of 2 x CUs, and
-  // a pair unit takes two one-head units' time: pairs pay only where
+  // A CU holds two one-head decode workgroups, so those run in rounds of
+  // 2 x CUs, and a pair unit takes two one-head units' time: pairs pay only where
   // 2 * rounds(pairs) <= rounds(one-head units).  Measured (one-head -> pair
   // units): +2 to +5% at head_dim 128 and +9 to +13% at 64 where both fill
   // whole rounds (e.g. 256 x 4096 MHA, 64 x 2048 with 32 heads of 64), but
@@ -209,11 +209,14 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
                     2 * cdiv(units1 / 2, per_round) <= cdiv(units1, per_round) && !pair_units_disabled()
                 ? 2
                 : 1;
-  pl.splits = a->num_splits > 0
-                  ? a->num_splits
-                  : paged_attn_num_splits(a->batch, a->total_q, a->num_heads_q / pl.pair,
-                                          a->num_heads_kv / pl.pair, a->head_dim, a->max_seqlen_q,
-                                          pl.max_seqlen_k, num_cus);
+  // Pair units arise only at two or more per CU, where whole key ranges beat
+  // split ones: the heuristic's two splits for uneven unit counts made pair
+  // units 7-10% slower (50 and 52 sequences x 32 heads, 200 x 8 kv heads).
+  pl.splits = a->num_splits > 0 ? a->num_splits
+              : pl.pair == 2    ? 1
+                                : paged_attn_num_splits(a->batch, a->total_q, a->num_heads_q,
+                                                        a->num_heads_kv, a->head_dim,
+                                                        a->max_seqlen_q, pl.max_seqlen_k, num_cus);
   // workgroups per kv head: one per decode unit (decode-only kernel); one per
   // prefill unit plus one per two decode units (unified kernel).  Decode
   // units number at most batch * splits; prefill units, the sum over the n_p
@@ -538,8 +541,9 @@ int32_t paged_attn_num_splits(int32_t batch, int32_t total_q, int32_t num_heads_
                               int32_t max_seqlen_k, int32_t num_cus) {
   // Host-only cost model (no device length is read).  Work units without any
   // split: one per (sequence, kv head) plus the prefill tiles.  Once they give
-  // every compute unit a workgroup, splitting only adds partial-result
-  // traffic and a combine.  Otherwise split each key range so the units reach
+  // every compute unit a workgroup, splitting mostly adds only partial-result
+  // traffic and a combine (the exception, uneven units, follows).  Otherwise
+  // split each key range so the units reach
   // one per compute unit, but keep at least 8 key tiles of 32 per split (two
   // per wave) so a split's fixed cost stays amortised, and stay within the
   // cap of 128.  A key range that allows only two such splits is halved only

@@ -122,6 +122,19 @@ def test_workspace_size_and_splits_for_are_host_only():
     assert pa.paged_attn_splits_for(valid_args(head_dim=96)) == -1
 
 
+def test_plan_keeps_pair_units_whole():
+    # 50 sequences x 32 kv heads at 4096 keys: the plan runs 800 units over
+    # pairs of kv heads and keeps them unsplit, though the heuristic alone
+    # would give 800 units two splits
+    kw = dict(total_q=50, max_seqlen_q=1, num_heads_q=32, num_heads_kv=32, head_dim=128,
+              max_seqlen_k=4096, num_pages=50 * 256, max_pages_per_seq=256)
+    assert pa.paged_attn_num_splits(50, 50, 16, 16, 128, 1, 4096, 256) == 2
+    assert pa.paged_attn_splits_for(valid_args(batch=50, **kw)) == 1
+    # 12 sequences: 384 one-head units, which take the heuristic's two splits
+    kw.update(total_q=12, num_pages=12 * 256)
+    assert pa.paged_attn_splits_for(valid_args(batch=12, **kw)) == 2
+
+
 def test_status_strings():
     for code in range(10):
         assert pa.paged_attn_status_string(code) != "unknown status"
