@@ -305,6 +305,48 @@ def sweep(name, reps, out_path):
                       "decode_only_frac": dby / (HBM_PEAK_GBS * 1e9) * 1e3 / dmed})
                 del inp, di, pi
                 torch.cuda.empty_cache()
+    elif name == "plan":
+        # the plan's unit shape and split budget on all-decode batches whose
+        # unit counts fall between whole multiples of the compute units,
+        # beside forced alternatives: one-head or pair units
+        # (PAGED_ATTN_HEAD_PAIRS=0 / 2), one or two splits; every sequence at
+        # `ctx` cached keys, no append
+        points = [(32, 32, 128, B, 4096) for B in (12, 20, 24, 40, 48, 50, 60, 96, 100)]
+        points += [(32, 32, 128, 12, 2048), (32, 32, 128, 20, 8192), (32, 32, 128, 52, 2048),
+                   (32, 8, 128, 48, 8192), (32, 8, 128, 200, 4096),
+                   (12, 12, 64, 96, 4096), (12, 12, 64, 128, 4096), (12, 12, 64, 200, 2048),
+                   (32, 32, 64, 128, 4096)]
+        env0 = os.environ.get("PAGED_ATTN_HEAD_PAIRS")
+        for hq, hkv, hd, B, ctx in points:
+            c = wl.Case(name=f"plan_{hq}x{hkv}x{hd}_b{B}_ctx{ctx}", q_lens=[1] * B,
+                        cache_seqlens=[ctx] * B, num_heads_q=hq, num_heads_kv=hkv, head_dim=hd,
+                        dtype="f16", page_size=16, append=False, causal=False,
+                        seed=6000 + B + ctx + hkv + hd)
+            inp = wl.make_inputs(c, "cuda")
+            by = algorithmic_bytes(c)
+            rec = {"sweep": "plan", "heads": f"{hq}/{hkv}", "head_dim": hd, "batch": B, "ctx": ctx,
+                   "units_one_head": B * hkv}
+            for label, pm, ns in (("plan", None, 0), ("one_S1", "0", 1), ("one_S2", "0", 2),
+                                  ("pairs_S1", "2", 1), ("pairs_S2", "2", 2)):
+                if pm is None:
+                    os.environ.pop("PAGED_ATTN_HEAD_PAIRS", None)
+                else:
+                    os.environ["PAGED_ATTN_HEAD_PAIRS"] = pm
+                S, med, mn = run(c, inp, num_splits=ns)
+                rec[label + "_ms"] = med
+                if label == "plan":
+                    rec.update({"plan_splits": S, "plan_GBps": by / med / 1e6,
+                                "plan_frac": by / med / 1e6 / HBM_PEAK_GBS})
+            if env0 is None:
+                os.environ.pop("PAGED_ATTN_HEAD_PAIRS", None)
+            else:
+                os.environ["PAGED_ATTN_HEAD_PAIRS"] = env0
+            forced = {k: rec[k + "_ms"] for k in ("one_S1", "one_S2", "pairs_S1", "pairs_S2")}
+            best = min(forced, key=forced.get)
+            rec.update({"best_forced": best, "plan_over_best": rec["plan_ms"] / forced[best]})
+            emit(rec)
+            del inp
+            torch.cuda.empty_cache()
     elif name == "multitoken":
         # decode with q_len new tokens per sequence (speculative scoring): one
         # decode unit per sequence while q_len * G <= 16; HBM rate vs q_len = 1
@@ -394,7 +436,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--sweep", choices=["copy", "decode", "gqa", "prefill", "unified", "graph", "rotary",
-                                        "multitoken"],
+                                        "multitoken", "plan"],
                     help="run a measurement sweep instead of the headline line")
     ap.add_argument("--sweep-out", default="sweep.jsonl")
     ap.add_argument("--reps", type=int, default=10)

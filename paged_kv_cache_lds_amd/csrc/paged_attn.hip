@@ -59,10 +59,14 @@ bool full_search_forced() {
   return e != nullptr && std::strcmp(e, "1") == 0;
 }
 
-// PAGED_ATTN_HEAD_PAIRS=0: decode units over one kv head only
-bool pair_units_disabled() {
+// PAGED_ATTN_HEAD_PAIRS=0: decode units over one kv head only; =2: over
+// pairs of kv heads wherever a pair's rows fit one unit (the size rules of
+// make_plan skipped); otherwise those rules decide
+int pair_mode() {
   const char *e = std::getenv("PAGED_ATTN_HEAD_PAIRS");
-  return e != nullptr && std::strcmp(e, "0") == 0;
+  if (e != nullptr && std::strcmp(e, "0") == 0) return 0;
+  if (e != nullptr && std::strcmp(e, "2") == 0) return 2;
+  return 1;
 }
 
 
@@ -204,19 +208,24 @@ Plan make_plan(const pa_fwd_args *a, int num_cus) {
   // 128 and 200 sequences x 12 heads).
   const long units1 = (long)a->batch * a->num_heads_kv;
   const long per_round = 2L * num_cus;
-  pl.pair = pl.all_decode && a->num_heads_kv % 2 == 0 &&
-                    2L * a->max_seqlen_q * group <= pa::kDecodeRows && units1 >= 4L * num_cus &&
-                    2 * cdiv(units1 / 2, per_round) <= cdiv(units1, per_round) && !pair_units_disabled()
-                ? 2
-                : 1;
-  // Pair units arise only at two or more per CU, where whole key ranges beat
-  // split ones: the heuristic's two splits for uneven unit counts made pair
-  // units 7-10% slower (50 and 52 sequences x 32 heads, 200 x 8 kv heads).
-  pl.splits = a->num_splits > 0 ? a->num_splits
-              : pl.pair == 2    ? 1
-                                : paged_attn_num_splits(a->batch, a->total_q, a->num_heads_q,
-                                                        a->num_heads_kv, a->head_dim,
-                                                        a->max_seqlen_q, pl.max_seqlen_k, num_cus);
+  const bool pair_fits = pl.all_decode && a->num_heads_kv % 2 == 0 &&
+                         2L * a->max_seqlen_q * group <= pa::kDecodeRows;
+  const bool pair_pays =
+      units1 >= 4L * num_cus && 2 * cdiv(units1 / 2, per_round) <= cdiv(units1, per_round);
+  const int pm = pair_mode();
+  pl.pair = pair_fits && (pm == 2 || (pm == 1 && pair_pays)) ? 2 : 1;
+  // Pair units that give every CU one keep their key ranges whole: the
+  // heuristic's two splits for uneven unit counts made them 7-10% slower (50
+  // and 52 sequences x 32 heads, 200 x 8 kv heads).  Fewer pair units (only
+  // with PAGED_ATTN_HEAD_PAIRS=2) take the heuristic over the pairs.
+  if (a->num_splits > 0)
+    pl.splits = a->num_splits;
+  else if (pl.pair == 2 && units1 / 2 >= num_cus)
+    pl.splits = 1;
+  else
+    pl.splits = paged_attn_num_splits(a->batch, a->total_q, a->num_heads_q / pl.pair,
+                                      a->num_heads_kv / pl.pair, a->head_dim, a->max_seqlen_q,
+                                      pl.max_seqlen_k, num_cus);
   // workgroups per kv head: one per decode unit (decode-only kernel); one per
   // prefill unit plus one per two decode units (unified kernel).  Decode
   // units number at most batch * splits; prefill units, the sum over the n_p
