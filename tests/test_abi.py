@@ -9,6 +9,7 @@ import subprocess
 import tempfile
 
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import paged_kv_cache_lds_amd as pa
 from paged_kv_cache_lds_amd import _build
@@ -233,3 +234,26 @@ def test_noalloc_entry_point_host_checks():
     # 2 rows with 4 splits is well within the array) - only sizes are compared
     small = valid_args(num_splits=4)
     assert 0 < pa.paged_attn_workspace_size(small) <= pa.NOALLOC_SCRATCH_BYTES
+
+
+@settings(max_examples=300, deadline=None)
+@given(batch=st.integers(1, 300), hkv=st.sampled_from([1, 2, 4, 8, 12, 16, 32]),
+       group=st.sampled_from([1, 2, 4, 8]), d=st.sampled_from([64, 128]),
+       q_len=st.integers(1, 40), ctx=st.integers(1, 200000), forced=st.sampled_from([0, 1, 3, 128]))
+def test_plan_queries_are_consistent(batch, hkv, group, d, q_len, ctx, forced):
+    # the host-only sizing queries over random shapes: a split count in
+    # [1, 128] (a forced one honoured), and a workspace exactly when a row
+    # can have partials
+    pages = -(-ctx // 16)
+    a = valid_args(batch=batch, total_q=batch * q_len, max_seqlen_q=q_len, num_heads_q=hkv * group,
+                   num_heads_kv=hkv, head_dim=d, max_seqlen_k=ctx, num_pages=batch * pages,
+                   max_pages_per_seq=pages, num_splits=forced)
+    s = pa.paged_attn_splits_for(a)
+    assert 1 <= s <= 128
+    if forced:
+        assert s == forced
+    ws = pa.paged_attn_workspace_size(a)
+    assert (ws > 0) == (s > 1)
+    if s > 1:
+        # every row of every split: an fp32 output row and its lse
+        assert ws >= s * batch * q_len * hkv * group * (d + 1) * 4
