@@ -143,6 +143,27 @@ def test_mha_decode_uneven_units_split_in_two(batch):
     run_fullsize(c, {0: [0], batch // 2: [0], batch - 1: [0]}, causal=False)
 
 
+def test_one_sequence_of_262144_keys():
+    # one sequence at 262143 cached keys plus one appended, 64 q / 8 kv heads,
+    # bf16, pages of 256: the one-sequence decode path with the heuristic's
+    # split budget over a quarter-million keys
+    c = wl.Case(name="one_seq_256k", q_lens=[1], cache_seqlens=[262143], num_heads_q=64,
+                num_heads_kv=8, head_dim=128, dtype="bf16", page_size=256, append=True,
+                causal=True, seed=7100)
+    run_fullsize(c, {0: [0]})
+
+
+def test_contiguous_allocation_at_the_2gib_limit():
+    # contiguous allocations of 2^20 - 32 rows of 8 kv heads x 128 (2 GiB less
+    # 64 KiB per sequence, under the 2^31-byte bound of 32-bit in-slab
+    # offsets); the first sequence fills its allocation after the append
+    alloc = (1 << 20) - 32
+    c = wl.Case(name="contig_2gib", q_lens=[1, 1], cache_seqlens=[alloc - 1, 1000], num_heads_q=8,
+                num_heads_kv=8, head_dim=128, dtype="f16", page_size=None, contig_alloc=alloc,
+                append=True, causal=True, seed=7101)
+    run_fullsize(c, {0: [0], 1: [0]})
+
+
 @pytest.mark.parametrize("paged", [True, False])
 def test_gqa_long_split_allocation_bound(paged):
     # batch 8, 64/8 heads, lengths in [2048, 32768] inside a 131072-token
