@@ -143,6 +143,15 @@ def test_mha_decode_uneven_units_split_in_two(batch):
     run_fullsize(c, {0: [0], batch // 2: [0], batch - 1: [0]}, causal=False)
 
 
+def test_causal_prefill_one_sequence_of_32768_tokens():
+    # one 32768-token chunk with an empty cache, 32 heads x 128, fp16, page
+    # 16, appended in the call: query tiles of up to 1024 key tiles
+    c = wl.Case(name="prefill_32k", q_lens=[32768], cache_seqlens=[0], num_heads_q=32,
+                num_heads_kv=32, head_dim=128, dtype="f16", page_size=16, append=True,
+                causal=True, seed=7102)
+    run_fullsize(c, {0: [0, 255, 256, 16383, 32766, 32767]})
+
+
 def test_one_sequence_of_262144_keys():
     # one sequence at 262143 cached keys plus one appended, 64 q / 8 kv heads,
     # bf16, pages of 256: the one-sequence decode path with the heuristic's
