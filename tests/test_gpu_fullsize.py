@@ -143,6 +143,16 @@ def test_mha_decode_uneven_units_split_in_two(batch):
     run_fullsize(c, {0: [0], batch // 2: [0], batch - 1: [0]}, causal=False)
 
 
+def test_causal_prefill_gqa_bf16_4x2048():
+    # grouped heads (32 q / 8 kv, four query heads packed per kv head, so a
+    # 256-row unit covers 64 tokens) in bf16 (probabilities split into high
+    # and low parts for the PV product), at the prefill bench size
+    c = wl.Case(name="prefill_gqa_bf16", q_lens=[2048] * 4, cache_seqlens=[0, 100, 511, 2048],
+                num_heads_q=32, num_heads_kv=8, head_dim=128, dtype="bf16", page_size=16,
+                append=True, causal=True, seed=7103)
+    run_fullsize(c, {0: [0, 63, 64, 2047], 2: [1000], 3: [0, 2047]})
+
+
 def test_causal_prefill_one_sequence_of_32768_tokens():
     # one 32768-token chunk with an empty cache, 32 heads x 128, fp16, page
     # 16, appended in the call: query tiles of up to 1024 key tiles
