@@ -153,6 +153,15 @@ def test_causal_prefill_gqa_bf16_4x2048():
     run_fullsize(c, {0: [0, 63, 64, 2047], 2: [1000], 3: [0, 2047]})
 
 
+def test_causal_prefill_d64_page256_4x2048():
+    # head_dim 64 (waves 0-3 load a tile's K blocks, waves 4-7 its V blocks),
+    # pages of 256 keys, cached prefixes of 0-511 keys, at the bench size
+    c = wl.Case(name="prefill_d64_p256", q_lens=[2048] * 4, cache_seqlens=[0, 17, 256, 511],
+                num_heads_q=16, num_heads_kv=16, head_dim=64, dtype="f16", page_size=256,
+                append=True, causal=True, seed=7104)
+    run_fullsize(c, {0: [0, 255, 256, 2047], 1: [1500], 3: [0, 2047]})
+
+
 def test_causal_prefill_one_sequence_of_32768_tokens():
     # one 32768-token chunk with an empty cache, 32 heads x 128, fp16, page
     # 16, appended in the call: query tiles of up to 1024 key tiles
