@@ -107,6 +107,46 @@ def run_rotary(case, rotary_dim, interleaved, rows=None, kind="angles", splits=(
         assert torch.equal(lse, lse2), f"{case.name}: fused rotary lse differs from pre-rotated"
 
 
+@pytest.mark.parametrize("make", [lambda: wl.causal_prefill_append(2048, "zero"),
+                                  lambda: wl.mha_decode(256, 4096, append=True)],
+                         ids=["prefill_4x2048", "decode_256x4096"])
+def test_rotary_full_size_equals_pre_rotated(make):
+    # the rotary sweep's prefill and decode points at full size: the fused
+    # call equals the plain kernels on queries and new keys the oracle
+    # rotated, bit for bit, and leaves the same pools (the appended keys are
+    # the oracle's rotated bits); the plain path itself is checked against
+    # the oracle at these sizes in test_gpu_fullsize.py
+    case = make()
+    say(f"case {case.name} seed {case.seed} full size, rotary_dim 128")
+    inp = make_inputs(case, "cuda")
+    cos, sin = wl.rotary_tables(max(case.keys_visible()) + 1, 128, case.dtype, kind="angles",
+                                seed=case.seed)
+    pos = orot.token_positions(host(inp.cache_seqlens), host(inp.cu_seqlens_q), appended=True,
+                               total=inp.q.shape[0])
+    q_rot = to_dev(orot.rotate_bits(host(inp.q), host(cos), host(sin), pos, dtype=case.dtype,
+                                    interleaved=False), inp.q)
+    kn_rot = to_dev(orot.rotate_bits(host(inp.k_new), host(cos), host(sin), pos, dtype=case.dtype,
+                                     interleaved=False), inp.k_new)
+    kc0, vc0 = inp.k_cache.clone(), inp.v_cache.clone()
+    out, lse = pa.paged_attn_fwd(
+        inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens, inp.cu_seqlens_q,
+        max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=inp.max_seqlen_k, k_new=inp.k_new,
+        v_new=inp.v_new, causal=case.causal, rotary_cos=cos, rotary_sin=sin)
+    torch.cuda.synchronize()
+    kc1, vc1 = inp.k_cache.clone(), inp.v_cache.clone()
+    inp.k_cache.copy_(kc0)
+    inp.v_cache.copy_(vc0)
+    out2, lse2 = pa.paged_attn_fwd(
+        q_rot, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens, inp.cu_seqlens_q,
+        max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=inp.max_seqlen_k, k_new=kn_rot,
+        v_new=inp.v_new, causal=case.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "fused rotary differs from pre-rotated"
+    assert torch.equal(kc1, inp.k_cache) and torch.equal(vc1, inp.v_cache), "pools differ"
+    del inp, kc0, vc0, kc1, vc1
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("interleaved", [False, True])
 def test_rotary_mha_decode_append(interleaved):
     run_rotary(wl.mha_decode(3, 700, append=True), 128, interleaved, splits=(None, 3))
