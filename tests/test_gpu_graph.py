@@ -16,6 +16,7 @@ import torch
 
 import oracle
 import paged_kv_cache_lds_amd as pa
+import workloads as wl
 from workloads import host
 
 pytestmark = pytest.mark.gpu
@@ -142,3 +143,59 @@ def test_graph_replays_match_eager_calls(aux):
             # unrelated eager work between replays
             x = torch.rand(1 << 20, device="cuda")
             assert float((x * 2).sum()) > 0
+
+
+@pytest.mark.parametrize("make", [lambda: wl.mha_decode(1, 512), lambda: wl.mha_decode(8, 1024),
+                                  lambda: wl.unified_varlen(100, heads=12, head_dim=64)],
+                         ids=["decode_1x512", "decode_8x1024", "unified_nq100_h12x64"])
+def test_graph_sweep_points_replay_bit_exact(make):
+    # the graph sweep's three points with the library's own split budget: a
+    # captured call replayed three times, with eager work and syncs between,
+    # gives the eager call's outputs and pools bit for bit
+    c = make()
+    inp = wl.make_inputs(c, "cuda")
+    out = torch.empty_like(inp.q)
+    lse = torch.empty(inp.q.shape[:2], dtype=torch.float32, device="cuda")
+    kn = inp.k_new if c.append else None
+    vn = inp.v_new if c.append else None
+    args = pa.make_args(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens,
+                        inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q,
+                        max_seqlen_k=inp.max_seqlen_k, k_new=kn, v_new=vn, causal=c.causal,
+                        num_splits=0, out=out, softmax_lse=lse)
+    ws = torch.empty(max(1, pa.paged_attn_workspace_size(args)), dtype=torch.uint8, device="cuda")
+    kc0, vc0 = inp.k_cache.clone(), inp.v_cache.clone()
+
+    def call():
+        pa.paged_attn_fwd(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.cache_seqlens,
+                          inp.cu_seqlens_q, max_seqlen_q=inp.max_seqlen_q,
+                          max_seqlen_k=inp.max_seqlen_k, k_new=kn, v_new=vn, causal=c.causal,
+                          out=out, softmax_lse=lse, workspace=ws)
+
+    def reset():
+        inp.k_cache.copy_(kc0)
+        inp.v_cache.copy_(vc0)
+        out.zero_()
+        lse.zero_()
+
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, lse, inp.k_cache, inp.v_cache)]
+    reset()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((out, lse, inp.k_cache, inp.v_cache), ref,
+                                   ("out", "lse", "k_cache", "v_cache")):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager call"
